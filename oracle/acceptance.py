@@ -1,0 +1,79 @@
+"""Greedy acceptance of a draft tree (oracle side).
+
+Definitions:
+
+* Greedy target token of node v: the index of the largest logit of node v's
+  row (hard matching in the verification step of Speculative Streaming; the
+  check of predictions at the lookahead positions in Lookahead Attention
+  section 2.3).  Row v verifies node v.  Ties go to the lowest index, and
+  -0 equals +0 (``numpy.argmax`` returns the first maximal entry).
+* Node v matches when its drafted token equals its greedy target token.  It
+  is accepted when it matches and so does every node on its path from the
+  root (a branch is followed until a rejection).  Its depth is the number of
+  nodes on that path; nodes with parent -1 hang off the root and have depth 1.
+  Nodes deeper than ``max_depth`` are never accepted (the caller's bound on
+  the path length).
+* The accepted length A is the largest depth of an accepted node (0 if none),
+  i.e. the longest accepted path; for a chain it is the leading run of
+  matches (Lookahead Attention section 2.4, longest consistent prefix).
+* When several accepted nodes reach depth A, the path is the one a
+  depth-first walk from the root meets first, visiting children in
+  increasing index order; that is the path whose node-index sequence is
+  lexicographically smallest.  ``path[d]`` is the node at depth d+1, and
+  entries past A are -1.
+"""
+
+from typing import Tuple
+
+import numpy as np
+
+from .bf16 import as_f64
+
+
+def greedy_tokens(logits: np.ndarray, logits_dtype: str) -> np.ndarray:
+    """Per-row argmax over the vocabulary (first maximal index). [B, T] int32."""
+    return np.argmax(as_f64(logits, logits_dtype), axis=-1).astype(np.int32)
+
+
+def accept_request(draft_tok, acc_parent, greedy, n_nodes: int, max_depth: int):
+    """Return (A, path[max_depth]) for one request."""
+    n = int(n_nodes)
+    depth = np.zeros(n, dtype=np.int64)
+    acc = np.zeros(n, dtype=bool)
+    for v in range(n):
+        p = int(acc_parent[v])
+        if p >= v:
+            raise ValueError("acceptance parents must precede their children")
+        ok = int(draft_tok[v]) == int(greedy[v])
+        depth[v] = 1 if p < 0 else depth[p] + 1
+        acc[v] = ok and (p < 0 or acc[p]) and depth[v] <= max_depth
+    path = np.full(max_depth, -1, dtype=np.int32)
+    if not acc.any():
+        return 0, path
+    A = int(depth[acc].max())
+    best = None
+    for v in range(n):
+        if acc[v] and depth[v] == A:
+            chain = []
+            u = v
+            while u >= 0:
+                chain.append(u)
+                u = int(acc_parent[u])
+            chain.reverse()
+            if best is None or chain < best:
+                best = chain
+    path[:A] = best
+    return A, path
+
+
+def argmax_accept(logits, logits_dtype: str, n_nodes, draft_tok, acc_parent,
+                  max_depth: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Batch form: (greedy [B, T], out_len [B], out_path [B, max_depth]), all int32."""
+    greedy = greedy_tokens(logits, logits_dtype)
+    B = greedy.shape[0]
+    out_len = np.zeros(B, dtype=np.int32)
+    out_path = np.full((B, max_depth), -1, dtype=np.int32)
+    for b in range(B):
+        out_len[b], out_path[b] = accept_request(draft_tok[b], acc_parent[b], greedy[b],
+                                                 int(n_nodes[b]), max_depth)
+    return greedy, out_len, out_path
