@@ -1,0 +1,247 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) verification step for
+ * self-speculative decoding.
+ *
+ * One decode iteration of self-speculative decoding runs the target model
+ * once over [cached prefix + a block of speculative tokens], accepts or
+ * rejects the drafts from the block's logits, and keeps only the accepted
+ * tokens' K/V.  This library implements the data-parallel parts of that step
+ * as hand-written HIP kernels:
+ *
+ *   spec_build_mask     parent array -> bit-packed block visibility mask
+ *   spec_verify_attn    attention of the block's queries over
+ *                       [soft prompt | cached prefix | block] under that mask
+ *   spec_argmax_accept  per-node greedy token, longest accepted path
+ *   spec_commit_kv      append the accepted nodes' K/V to the cache
+ *
+ * Sources (page titles; sections, equations):
+ *   [LA] "Lookahead Attention: Self-Speculative Verification via Parallel
+ *        Token Proposals" -- 2.1 dual-stream mask, 2.3/2.4 verification and
+ *        longest consistent prefix, 3.1 M_LA, 3.2 KV discarded, 3.3 padding.
+ *   [CF] "ConFu: Contemplate the Future for Better Speculative Sampling" --
+ *        key design 1: soft prompt in the KV cache visible only to
+ *        contemplate tokens; one contemplate token per tree node (2T rows).
+ *   [SS] "Speculative Streaming: Fast LLM Inference without Auxiliary
+ *        Models" -- Equation 1 (attention, 1/sqrt(d) scale), tree draft and
+ *        Equation 4 (each node sees its root-to-node path), the verification
+ *        step (depth-first, hard matching, longest accepted path), lazy KV
+ *        garbage collection after the step.
+ *
+ * Conventions (all entry points):
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *     stated otherwise.  The library allocates no memory and keeps no state
+ *     between calls; calls are reentrant.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; the functions never synchronise.  Values that
+ *     depend on data (accepted lengths and paths, cache lengths) stay on the
+ *     device, so the calls chain on one stream without a host round trip.
+ *   - Return value: SPEC_OK, or a negative spec_status.  Shapes, dtypes,
+ *     pointers and alignment are validated on the host BEFORE anything is
+ *     enqueued; on failure nothing is enqueued.  spec_last_error() returns a
+ *     thread-local description of the most recent failure in this thread.
+ *   - Contents of device arrays (parents, lengths, token ids) cannot be
+ *     checked on the host; they are preconditions stated per function.  The
+ *     kernels clamp every index they derive from such data, so a violated
+ *     precondition gives unspecified results but never an out-of-bounds
+ *     access.
+ *   - bf16 is IEEE-style bfloat16 (the upper 16 bits of a float32).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_F32 = 0,   /* float32  */
+  SPEC_BF16 = 1   /* bfloat16 */
+} spec_dtype;
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,        /* bad argument: null pointer, bad shape, misaligned */
+  SPEC_EUNSUPPORTED = -2,  /* valid request outside what the kernels implement */
+  SPEC_EWORKSPACE = -3,    /* workspace missing or smaller than required       */
+  SPEC_EHIP = -4           /* the HIP runtime reported an error                */
+} spec_status;
+
+/* Limits of this implementation. */
+#define SPEC_MAX_TQ 256        /* query rows per request in the block      */
+#define SPEC_MAX_NODES 256     /* acceptance nodes per request             */
+#define SPEC_MAX_DEPTH 16      /* longest accepted path                    */
+#define SPEC_MAX_SOFT 256      /* soft-prompt rows                          */
+
+/* Shape and layout of one verify-attention call (one transformer layer). */
+typedef struct {
+  int32_t B;       /* requests                                                */
+  int32_t Tq;      /* query rows of the speculative block per request (<=256) */
+  int32_t Hq;      /* query heads                                             */
+  int32_t Hkv;     /* key/value heads; Hq % Hkv == 0; q-head j reads kv-head
+                      j / (Hq / Hkv) (contiguous groups)                      */
+  int32_t D;       /* head dimension: 64 or 128                               */
+  int32_t S;       /* soft-prompt rows (0 = none)                             */
+  int32_t dtype;   /* spec_dtype of q, caches, block and soft K/V             */
+  float scale;     /* softmax scale; 0 selects 1/sqrt(D) ([SS] Equation 1)    */
+  int64_t lmax;    /* cache capacity in rows per request                      */
+  int64_t kv_stride_b, kv_stride_l, kv_stride_h; /* element strides of the
+                      caches for request, row and head; D is contiguous.
+                      [B, lmax, Hkv, D] contiguous: (lmax*Hkv*D, Hkv*D, D);
+                      [B, Hkv, lmax, D] contiguous: (Hkv*lmax*D, D, lmax*D). */
+  int32_t kv_splits; /* 0 = automatic; else split each request's prefix into
+                        this many key ranges (tuning and testing)             */
+  int32_t reserved;  /* must be 0                                             */
+} spec_attn_desc;
+
+/*
+ * spec_build_mask -- bit-packed visibility of block keys for each query row.
+ *
+ * Row r of request b sees block key c iff r < n_q[b] and (c == r or c is an
+ * ancestor of r through attn_parent).  This one rule gives every mask of the
+ * sources: [SS] tree (a node sees its root-to-node path and no other branch;
+ * the printed Equation 4 is read through its prose, self included), [LA]
+ * M_LA (originals as a chain, lookahead rows hanging off the last original:
+ * causal originals, lookahead rows see the originals and themselves only;
+ * with the originals cached, all parents are -1: prefix + self), [CF]
+ * contemplate rows (parent = their node: the node's path, the node, itself).
+ * Every valid row also sees the whole cached prefix (implicit, not stored).
+ *
+ *   attn_parent [B, Tq] int32   parent row, -1 = hangs off the prefix.
+ *                               Precondition: -1 <= attn_parent[b][r] < r.
+ *                               A link that breaks it ends the walk.
+ *   sp_flag     [B, Tq] uint8   nonzero = the row sees the soft prompt
+ *                               ([CF] contemplate rows); NULL = no row does.
+ *   n_q         [B] int32       valid rows per request; rows r >= n_q[b] are
+ *                               batch padding ([LA] 3.3) and see nothing.
+ *                               Clamped to [0, Tq].
+ *   mask_bits   [B, Tq, W] uint32 out, W = ceil(Tq/32): bit (c % 32) of
+ *                               word c / 32 is key c; unused high bits are 0.
+ *   sp_bits     [B, W] uint32   out: bit r = row r sees the soft prompt.
+ *
+ * Limits: 1 <= Tq <= 256.  B == 0 is a no-op.
+ */
+int spec_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag, const int32_t* n_q,
+                    int32_t B, int32_t Tq, uint32_t* mask_bits, uint32_t* sp_bits,
+                    void* stream);
+
+/*
+ * spec_verify_attn_workspace -- bytes of device workspace spec_verify_attn
+ * needs for this descriptor (0 if none).  Returns 0 for an invalid
+ * descriptor as well; spec_verify_attn reports the error.
+ */
+size_t spec_verify_attn_workspace(const spec_attn_desc* d);
+
+/*
+ * spec_verify_attn -- masked attention of the speculative block.
+ *
+ * For request b, valid row r (< n_q[b]) and query head j (kv-head
+ * h = j / (Hq/Hkv)), over the keys the row sees:
+ *   soft keys s < S        iff bit r of sp_bits[b]              ([CF])
+ *   prefix keys l < L_b    always, L_b = cache_len[b]          ([LA], [SS])
+ *   block keys c < Tq      iff bit c of mask_bits[b][r]        (spec_build_mask)
+ * out[b,r,j,:] = sum_k softmax_k(scale * <q, k>) v_k              ([SS] Eq. 1)
+ * lse[b,r,j]   = natural log of sum_k exp(scale * <q, k>).
+ * Padded rows (r >= n_q[b]) get out = 0 and lse = -inf.
+ *
+ *   q        [B, Tq, Hq, D] dtype, contiguous
+ *   k_cache, v_cache  cache rows per the descriptor's strides; only rows
+ *            [0, L_b) are read.  Precondition: 0 <= cache_len[b] <= lmax
+ *            (clamped).
+ *   k_blk, v_blk  [B, Tq, Hkv, D] dtype, contiguous: the block's own K/V
+ *   k_soft, v_soft [S, Hkv, D] dtype, shared by all requests; NULL iff S == 0
+ *   mask_bits [B, Tq, W], sp_bits [B, W] as produced by spec_build_mask
+ *            (sp_bits may be NULL iff S == 0)
+ *   n_q      [B] int32, clamped to [0, Tq]
+ *   out      [B, Tq, Hq, D] float32
+ *   lse      [B, Tq, Hq] float32, or NULL
+ *   workspace  device buffer of at least spec_verify_attn_workspace(d)
+ *            bytes (may be NULL when that is 0).  Contents need no
+ *            initialisation and are scratch after the call.
+ *
+ * Computation: fp32 accumulation; bf16 inputs use bf16 MFMA for QK^T and PV
+ * (probabilities rounded to bf16 for PV) when (Hq/Hkv)*Tq >= 16, and fp32
+ * VALU arithmetic otherwise.  Alignment: all tensors 16-byte aligned, and
+ * the strides a multiple of 16 bytes.
+ * Limits: D in {64, 128}; 1 <= Tq <= 256; 0 <= S <= 256; B == 0 is a no-op.
+ */
+int spec_verify_attn(const spec_attn_desc* d, const void* q,
+                     const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                     const void* k_blk, const void* v_blk,
+                     const void* k_soft, const void* v_soft,
+                     const uint32_t* mask_bits, const uint32_t* sp_bits, const int32_t* n_q,
+                     float* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * spec_argmax_accept -- greedy verification of a draft tree.
+ *
+ * For node v < n_nodes[b] ([SS] verification step, hard matching; [LA] 2.3):
+ *   out_argmax[b][v] = index of the largest logits[b][v][:] (lowest index
+ *                      on ties; -0 == +0; logits must not be NaN)
+ *   match(v)  = draft_tok[b][v] == out_argmax[b][v]
+ *   accepted(v) = match(v) and (acc_parent[b][v] == -1 or accepted(parent)),
+ *                 and depth(v) <= max_depth (depth 1 for parent -1)
+ *   out_len[b]  = largest depth of an accepted node, 0 if none
+ *                 (the longest accepted path; [LA] 2.4 longest prefix)
+ *   out_path[b][d] = node at depth d+1 on the accepted path that a
+ *                 depth-first walk from the root (children in increasing
+ *                 index) reaches first; -1 for d >= out_len[b].
+ * Row v of logits verifies node v.  Entries out_argmax[b][v] for
+ * v >= n_nodes[b] are -1.
+ *
+ *   logits     [B, T, V] logits_dtype, contiguous
+ *   n_nodes    [B] int32, clamped to [0, T]
+ *   draft_tok, acc_parent [B, T] int32.  Precondition: -1 <= acc_parent[b][v] < v.
+ *   out_argmax [B, T] int32 out; out_len [B] int32 out;
+ *   out_path   [B, max_depth] int32 out.
+ * Limits: 1 <= T <= 256; 1 <= V < 2^31; 1 <= max_depth <= 16; B == 0 is a no-op.
+ */
+int spec_argmax_accept(const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,
+                       const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
+                       int32_t max_depth, int32_t* out_argmax, int32_t* out_len,
+                       int32_t* out_path, void* stream);
+
+/*
+ * spec_commit_kv -- keep the accepted tokens' K/V ([SS] lazy garbage
+ * collection after the step; [LA] 3.2: callers of the lookahead form commit
+ * nothing, since lookahead K/V is dropped after the pass).
+ *
+ * For request b with L = cache_len_in[b] and A = out_len[b]:
+ *   for d < A with L + d < lmax:
+ *     cache[b, L + d, :, :] = blk[b, out_path[b][d], :, :]   (K and V)
+ *   cache_len_out[b] = L + (number of rows written).
+ * Every other cache row is left untouched.  Node v is block row v.
+ *
+ *   d          the descriptor used for spec_verify_attn (B, Tq, Hkv, D,
+ *              dtype, lmax and strides are used)
+ *   k_cache, v_cache  in/out caches
+ *   cache_len_in [B] int32; cache_len_out [B] int32 out (may alias
+ *              cache_len_in for an in-place update)
+ *   k_blk, v_blk [B, Tq, Hkv, D]
+ *   out_len [B], out_path [B, max_depth] as produced by spec_argmax_accept.
+ *              Path entries outside [0, Tq) are skipped.
+ * Limits: 1 <= max_depth <= 16.  B == 0 is a no-op.
+ */
+int spec_commit_kv(const spec_attn_desc* d, void* k_cache, void* v_cache,
+                   const int32_t* cache_len_in, int32_t* cache_len_out,
+                   const void* k_blk, const void* v_blk,
+                   const int32_t* out_len, const int32_t* out_path, int32_t max_depth,
+                   void* stream);
+
+/* Static description of a status code. */
+const char* spec_strerror(int status);
+
+/* Thread-local detail of the last failure in this thread ("" if none). */
+const char* spec_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* spec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,160 @@
+"""Thin ctypes binding of ``libspecverify.so`` (the C ABI in include/spec_verify.h).
+
+Argument marshalling only: every function forwards to the entry point of the
+same name.  Array arguments may be torch tensors (their ``data_ptr()`` is
+passed), plain integer addresses, or None (NULL).  ``stream`` defaults to
+torch's current HIP stream on the current device.  A non-zero status raises
+``SpecError`` carrying the library's own message.
+
+There is no fallback: if the HIP library is not built, the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_OK = 0
+SPEC_EINVAL = -1
+SPEC_EUNSUPPORTED = -2
+SPEC_EWORKSPACE = -3
+SPEC_EHIP = -4
+SPEC_MAX_TQ = 256
+SPEC_MAX_NODES = 256
+SPEC_MAX_DEPTH = 16
+SPEC_MAX_SOFT = 256
+
+# every symbol the header declares
+EXPORTS = ("spec_build_mask", "spec_verify_attn_workspace", "spec_verify_attn", "spec_argmax_accept",
+           "spec_commit_kv", "spec_strerror", "spec_last_error", "spec_version")
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func} failed with status {status}: {detail}")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("S", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("lmax", ctypes.c_int64), ("kv_stride_b", ctypes.c_int64), ("kv_stride_l", ctypes.c_int64),
+        ("kv_stride_h", ctypes.c_int64), ("kv_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m masked_verification_attention_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.spec_build_mask.argtypes = [_P, _P, _P, _I, _I, _P, _P, _P]
+    lib.spec_build_mask.restype = ctypes.c_int
+    lib.spec_verify_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.spec_verify_attn_workspace.restype = ctypes.c_size_t
+    lib.spec_verify_attn.argtypes = [ctypes.POINTER(AttnDesc)] + [_P] * 14 + [ctypes.c_size_t, _P]
+    lib.spec_verify_attn.restype = ctypes.c_int
+    lib.spec_argmax_accept.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P]
+    lib.spec_argmax_accept.restype = ctypes.c_int
+    lib.spec_commit_kv.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _I, _P]
+    lib.spec_commit_kv.restype = ctypes.c_int
+    lib.spec_strerror.argtypes = [ctypes.c_int]
+    lib.spec_strerror.restype = ctypes.c_char_p
+    lib.spec_last_error.argtypes = []
+    lib.spec_last_error.restype = ctypes.c_char_p
+    lib.spec_version.argtypes = []
+    lib.spec_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, func: str):
+    if status != SPEC_OK:
+        raise SpecError(status, func, load().spec_last_error().decode())
+
+
+def make_desc(B, Tq, Hq, Hkv, D, S, dtype, lmax, strides, scale=0.0, kv_splits=0) -> AttnDesc:
+    sb, sl, sh = strides
+    return AttnDesc(B, Tq, Hq, Hkv, D, S, dtype, scale, lmax, sb, sl, sh, kv_splits, 0)
+
+
+def spec_build_mask(attn_parent, sp_flag, n_q, B, Tq, mask_bits, sp_bits, stream=None):
+    lib = load()
+    _check(lib.spec_build_mask(_ptr(attn_parent), _ptr(sp_flag), _ptr(n_q), B, Tq, _ptr(mask_bits),
+                               _ptr(sp_bits), _stream(stream) if B else None), "spec_build_mask")
+
+
+def spec_verify_attn_workspace(desc: AttnDesc) -> int:
+    return int(load().spec_verify_attn_workspace(ctypes.byref(desc)))
+
+
+def spec_verify_attn(desc: AttnDesc, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft,
+                     mask_bits, sp_bits, n_q, out, lse=None, workspace=None, workspace_bytes=0,
+                     stream=None):
+    lib = load()
+    _check(lib.spec_verify_attn(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len),
+                                _ptr(k_blk), _ptr(v_blk), _ptr(k_soft), _ptr(v_soft), _ptr(mask_bits),
+                                _ptr(sp_bits), _ptr(n_q), _ptr(out), _ptr(lse), _ptr(workspace),
+                                int(workspace_bytes), _stream(stream) if desc.B else None),
+           "spec_verify_attn")
+
+
+def spec_argmax_accept(logits, logits_dtype, B, T, V, n_nodes, draft_tok, acc_parent, max_depth,
+                       out_argmax, out_len, out_path, stream=None):
+    lib = load()
+    _check(lib.spec_argmax_accept(_ptr(logits), logits_dtype, B, T, V, _ptr(n_nodes), _ptr(draft_tok),
+                                  _ptr(acc_parent), max_depth, _ptr(out_argmax), _ptr(out_len),
+                                  _ptr(out_path), _stream(stream) if B else None),
+           "spec_argmax_accept")
+
+
+def spec_commit_kv(desc: AttnDesc, k_cache, v_cache, cache_len_in, cache_len_out, k_blk, v_blk, out_len,
+                   out_path, max_depth, stream=None):
+    lib = load()
+    _check(lib.spec_commit_kv(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len_in),
+                              _ptr(cache_len_out), _ptr(k_blk), _ptr(v_blk), _ptr(out_len), _ptr(out_path),
+                              max_depth, _stream(stream) if desc.B else None),
+           "spec_commit_kv")
+
+
+def spec_strerror(status: int) -> str:
+    return load().spec_strerror(status).decode()
+
+
+def spec_last_error() -> str:
+    return load().spec_last_error().decode()
+
+
+def spec_version() -> str:
+    return load().spec_version().decode()

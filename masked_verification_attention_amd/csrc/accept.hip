@@ -1,0 +1,255 @@
+// Greedy acceptance of a draft tree.
+//
+// k_argmax: the greedy target token of every node -- the index of its row's
+// largest logit ("Speculative Streaming", the verification step: hard
+// matching against the target's most likely token; "Lookahead Attention"
+// 2.3).  One workgroup per node row streams the vocabulary with 16-byte loads;
+// each thread keeps its best (value, index) in increasing index order, and
+// the workgroup reduces with the rule "larger value, then lower index", so
+// ties resolve to the lowest index and -0 compares equal to +0.
+//
+// k_accept: one workgroup per request, one thread per node.  Each thread
+// walks its node's path to the root: the node is accepted iff every node on
+// the path matches its draft and the path is no longer than max_depth.  The
+// accepted length is the largest accepted depth ("Speculative Streaming":
+// the longest accepted path; "Lookahead Attention" 2.4: the longest
+// consistent prefix of a chain).  Among the deepest accepted nodes the path a
+// depth-first walk meets first (children in increasing index) is the one
+// with the lexicographically smallest root-first index sequence; node indices
+// are < 256 and paths are <= 16 long, so a path packs into a 128-bit key
+// (8 bits per depth, root in the top byte) and a min-reduction finds it.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace sv {
+
+constexpr int kArgThreads = 256;
+
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float elem_at(const T* p, int i);
+template <>
+__device__ __forceinline__ float elem_at<float>(const float* p, int i) { return p[i]; }
+template <>
+__device__ __forceinline__ float elem_at<uint16_t>(const uint16_t* p, int i) {
+  return __uint_as_float(uint32_t(p[i]) << 16);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ logits, int T_, int V,
+                                                        const int32_t* __restrict__ n_nodes,
+                                                        int32_t* __restrict__ out) {
+  constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
+  __shared__ float sv_[kArgThreads / kWave];
+  __shared__ int si_[kArgThreads / kWave];
+  const int row = blockIdx.x;
+  const int b = row / T_;
+  const int v = row % T_;
+  const int n = clampi(n_nodes[b], 0, T_);
+  if (v >= n) {
+    if (threadIdx.x == 0) out[row] = -1;
+    return;
+  }
+  const T* base = logits + (int64_t)row * V;
+  const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
+  const int pre = min(V, mis == 0 ? 0 : E - mis);
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < pre; i += kArgThreads) better(bv, bi, elem_at<T>(base, i), i);
+  const int nvec = (V - pre) / E;
+  const char* vb = reinterpret_cast<const char*>(base + pre);
+  constexpr int U = 4;
+  int k = threadIdx.x;
+  for (; k + (U - 1) * kArgThreads < nvec; k += U * kArgThreads) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = ldg16(vb + (int64_t)(k + u * kArgThreads) * 16);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i0 = pre + (k + u * kArgThreads) * E;
+      const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          better(bv, bi, bf16lo(w[e]), i0 + 2 * e);
+          better(bv, bi, bf16hi(w[e]), i0 + 2 * e + 1);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) better(bv, bi, __uint_as_float(w[e]), i0 + e);
+      }
+    }
+  }
+  for (; k < nvec; k += kArgThreads) {
+    const u32x4 x = ldg16(vb + (int64_t)k * 16);
+    const int i0 = pre + k * E;
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        better(bv, bi, bf16lo(w[e]), i0 + 2 * e);
+        better(bv, bi, bf16hi(w[e]), i0 + 2 * e + 1);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) better(bv, bi, __uint_as_float(w[e]), i0 + e);
+    }
+  }
+  for (int i = pre + nvec * E + threadIdx.x; i < V; i += kArgThreads) better(bv, bi, elem_at<T>(base, i), i);
+
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    better(bv, bi, ov, oi);
+  }
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) {
+    sv_[wave] = bv;
+    si_[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kArgThreads / kWave; ++w) better(bv, bi, sv_[w], si_[w]);
+    out[row] = bi;
+  }
+}
+
+constexpr int kAccThreads = 256;   // >= SPEC_MAX_NODES: one thread per node
+
+__device__ __forceinline__ bool key_less(uint64_t ah, uint64_t al, uint64_t bh, uint64_t bl) {
+  return ah < bh || (ah == bh && al < bl);
+}
+
+__global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* __restrict__ n_nodes,
+                                                        const int32_t* __restrict__ draft_tok,
+                                                        const int32_t* __restrict__ acc_parent,
+                                                        const int32_t* __restrict__ argmax, int max_depth,
+                                                        int32_t* __restrict__ out_len,
+                                                        int32_t* __restrict__ out_path) {
+  __shared__ int32_t par[SPEC_MAX_NODES];
+  __shared__ uint8_t okv[SPEC_MAX_NODES];
+  __shared__ int red_i[kAccThreads / kWave];
+  __shared__ uint64_t red_h[kAccThreads / kWave];
+  __shared__ uint64_t red_l[kAccThreads / kWave];
+  __shared__ uint8_t lists[kAccThreads][SPEC_MAX_DEPTH];
+  const int b = blockIdx.x;
+  const int v = threadIdx.x;
+  const int n = clampi(n_nodes[b], 0, T_);
+  const int wave = v / kWave;
+  const int lane = v % kWave;
+  if (v < n) {
+    par[v] = acc_parent[(int64_t)b * T_ + v];
+    okv[v] = draft_tok[(int64_t)b * T_ + v] == argmax[(int64_t)b * T_ + v] ? 1 : 0;
+  }
+  __syncthreads();
+
+  // walk to the root; list[] holds the path bottom-up
+  int depth = 0;
+  bool acc = false;
+  uint8_t* list = lists[v];
+  if (v < n) {
+    int cur = v;
+    bool good = true;
+    while (cur >= 0) {
+      if (depth >= max_depth || !okv[cur]) {
+        good = false;
+        break;
+      }
+      list[depth++] = (uint8_t)cur;
+      const int p = par[cur];
+      if (p < -1 || p >= cur) {   // broken link: not a path to the root
+        good = false;
+        break;
+      }
+      cur = p;
+    }
+    acc = good;
+  }
+
+  // A = deepest accepted node
+  int a_len = acc ? depth : 0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a_len = max(a_len, __shfl_xor(a_len, o));
+  if (lane == 0) red_i[wave] = a_len;
+  __syncthreads();
+  a_len = 0;
+  for (int w = 0; w < kAccThreads / kWave; ++w) a_len = max(a_len, red_i[w]);
+
+  // lexicographically smallest root-first path among accepted nodes of depth A
+  uint64_t kh = ~0ull, kl = ~0ull;
+  if (acc && depth == a_len && a_len > 0) {
+    kh = 0ull;
+    kl = 0ull;
+    for (int d = 0; d < depth; ++d) {
+      const uint64_t node = (uint64_t)list[depth - 1 - d];
+      if (d < 8) kh |= node << (56 - 8 * d);
+      else kl |= node << (56 - 8 * (d - 8));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t oh = __shfl_xor(kh, o);
+    const uint64_t ol = __shfl_xor(kl, o);
+    if (key_less(oh, ol, kh, kl)) {
+      kh = oh;
+      kl = ol;
+    }
+  }
+  if (lane == 0) {
+    red_h[wave] = kh;
+    red_l[wave] = kl;
+  }
+  __syncthreads();
+  if (v == 0) {
+    for (int w = 1; w < kAccThreads / kWave; ++w)
+      if (key_less(red_h[w], red_l[w], kh, kl)) {
+        kh = red_h[w];
+        kl = red_l[w];
+      }
+    out_len[b] = a_len;
+  }
+  __syncthreads();
+  if (v == 0) {
+    red_h[0] = kh;
+    red_l[0] = kl;
+  }
+  __syncthreads();
+  if (v < max_depth) {
+    int node = -1;
+    if (v < a_len) {
+      const uint64_t w = v < 8 ? red_h[0] : red_l[0];
+      const int sh = 56 - 8 * (v & 7);
+      node = (int)((w >> sh) & 0xffull);
+    }
+    out_path[(int64_t)b * max_depth + v] = node;
+  }
+}
+
+hipError_t launch_argmax(const void* logits, int dtype, int B, int T, int V, const int32_t* n_nodes,
+                         int32_t* out_argmax, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)B * T));
+  if (dtype == SPEC_F32)
+    hipLaunchKernelGGL(k_argmax<float>, grid, dim3(kArgThreads), 0, st, static_cast<const float*>(logits), T,
+                       V, n_nodes, out_argmax);
+  else
+    hipLaunchKernelGGL(k_argmax<uint16_t>, grid, dim3(kArgThreads), 0, st,
+                       static_cast<const uint16_t*>(logits), T, V, n_nodes, out_argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(int B, int T, const int32_t* n_nodes, const int32_t* draft_tok,
+                         const int32_t* acc_parent, const int32_t* argmax, int max_depth,
+                         int32_t* out_len, int32_t* out_path, hipStream_t st) {
+  hipLaunchKernelGGL(k_accept, dim3(B), dim3(kAccThreads), 0, st, T, n_nodes, draft_tok, acc_parent, argmax,
+                     max_depth, out_len, out_path);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,281 @@
+// C ABI of the verification step: argument validation, scheduling, launch.
+//
+// Every check here runs on the host before anything is enqueued, so a
+// rejected call leaves the stream untouched.  The checks make no HIP call
+// and do not touch device memory: they are exercised without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return SPEC_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SPEC_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int esize_of(int dtype) { return dtype == SPEC_F32 ? 4 : 2; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+// Descriptor checks shared by spec_verify_attn, its workspace query and spec_commit_kv.
+int check_desc(const spec_attn_desc* d) {
+  REQUIRE(d != nullptr, SPEC_EINVAL, "descriptor is NULL");
+  REQUIRE(d->B >= 0, SPEC_EINVAL, "B = %d < 0", d->B);
+  REQUIRE(d->Tq >= 1 && d->Tq <= SPEC_MAX_TQ, SPEC_EINVAL, "Tq = %d outside [1, %d]", d->Tq, SPEC_MAX_TQ);
+  REQUIRE(d->Hq >= 1 && d->Hkv >= 1, SPEC_EINVAL, "Hq = %d, Hkv = %d must be >= 1", d->Hq, d->Hkv);
+  REQUIRE(d->Hq % d->Hkv == 0, SPEC_EINVAL, "Hq = %d is not a multiple of Hkv = %d", d->Hq, d->Hkv);
+  REQUIRE(d->dtype == SPEC_F32 || d->dtype == SPEC_BF16, SPEC_EINVAL, "dtype = %d is not a spec_dtype",
+          d->dtype);
+  REQUIRE(d->D == 64 || d->D == 128, SPEC_EUNSUPPORTED, "D = %d (supported: 64, 128)", d->D);
+  REQUIRE(d->S >= 0 && d->S <= SPEC_MAX_SOFT, SPEC_EINVAL, "S = %d outside [0, %d]", d->S, SPEC_MAX_SOFT);
+  REQUIRE(d->lmax >= 0 && d->lmax < (int64_t(1) << 31), SPEC_EINVAL, "lmax = %lld outside [0, 2^31)",
+          (long long)d->lmax);
+  REQUIRE(d->kv_stride_b > 0 && d->kv_stride_l > 0 && d->kv_stride_h > 0, SPEC_EINVAL,
+          "cache strides must be positive");
+  const int64_t es = esize_of(d->dtype);
+  REQUIRE((d->kv_stride_b * es) % 16 == 0 && (d->kv_stride_l * es) % 16 == 0 && (d->kv_stride_h * es) % 16 == 0,
+          SPEC_EINVAL, "cache strides must be multiples of 16 bytes");
+  REQUIRE(d->kv_stride_h >= d->D || d->Hkv == 1, SPEC_EINVAL, "kv_stride_h < D would overlap heads");
+  REQUIRE(d->kv_splits >= 0 && d->kv_splits <= 64, SPEC_EINVAL, "kv_splits = %d outside [0, 64]", d->kv_splits);
+  REQUIRE(d->reserved == 0, SPEC_EINVAL, "reserved field must be 0");
+  REQUIRE(isfinite(d->scale) && d->scale >= 0.f, SPEC_EINVAL, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  REQUIRE((int64_t)d->B * d->Hkv <= 65535, SPEC_EUNSUPPORTED, "B * Hkv = %lld exceeds 65535",
+          (long long)((int64_t)d->B * d->Hkv));
+  return SPEC_OK;
+}
+
+}  // namespace
+
+namespace sv {
+
+AttnPlan plan_attn(const spec_attn_desc& d) {
+  AttnPlan p{};
+  const int G = d.Hq / d.Hkv;
+  const int R = G * d.Tq;
+  const int64_t items_bh = (int64_t)d.B * d.Hkv;
+  const int kCUs = 256;
+  if (d.dtype == SPEC_BF16 && R >= 16) {
+    p.path = PATH_MFMA;
+    p.rows_per_wg = R > 64 ? 128 : 64;
+    p.row_chunks = (R + p.rows_per_wg - 1) / p.rows_per_wg;
+    const int64_t items = items_bh * p.row_chunks;
+    int n = 1;
+    if (d.kv_splits > 0) {
+      n = d.kv_splits;
+    } else if (items < kCUs) {
+      // fill the chip, but keep at least 512 prefix keys per split
+      n = (int)((kCUs + items - 1) / items);
+      const int cap = (int)(d.lmax / 512 > 0 ? d.lmax / 512 : 1);
+      n = n < cap ? n : cap;
+    }
+    p.n_split = n < 1 ? 1 : n;
+  } else {
+    p.path = PATH_VALU;
+    p.rows_per_wg = 0;
+    p.row_chunks = 1;
+    int n = 1;
+    if (d.kv_splits > 0) {
+      n = d.kv_splits;
+    } else {
+      // ~512 prefix keys per workgroup: balances ragged prefixes, small partials
+      n = (int)((d.lmax + 511) / 512);
+      if (n < 1) n = 1;
+      if (n > 16) n = 16;
+    }
+    p.n_split = n;
+  }
+  if (p.n_split > 1) {
+    const size_t rows = (size_t)p.n_split * d.B * d.Hkv * R;
+    p.ws_bytes = rows * d.D * sizeof(float) + rows * 2 * sizeof(float) + 256;
+  }
+  return p;
+}
+
+}  // namespace sv
+
+extern "C" {
+
+const char* spec_version(void) { return "0.1.0"; }
+
+const char* spec_last_error(void) { return g_last_error; }
+
+const char* spec_strerror(int status) {
+  switch (status) {
+    case SPEC_OK: return "success";
+    case SPEC_EINVAL: return "invalid argument";
+    case SPEC_EUNSUPPORTED: return "unsupported configuration";
+    case SPEC_EWORKSPACE: return "workspace missing or too small";
+    case SPEC_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int spec_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag, const int32_t* n_q, int32_t B,
+                    int32_t Tq, uint32_t* mask_bits, uint32_t* sp_bits, void* stream) {
+  REQUIRE(B >= 0, SPEC_EINVAL, "B = %d < 0", B);
+  REQUIRE(Tq >= 1 && Tq <= SPEC_MAX_TQ, SPEC_EINVAL, "Tq = %d outside [1, %d]", Tq, SPEC_MAX_TQ);
+  if (B == 0) return ok();
+  REQUIRE(attn_parent && n_q && mask_bits && sp_bits, SPEC_EINVAL,
+          "attn_parent, n_q, mask_bits and sp_bits must be non-NULL");
+  REQUIRE(aligned(attn_parent, 4) && aligned(n_q, 4) && aligned(mask_bits, 4) && aligned(sp_bits, 4),
+          SPEC_EINVAL, "int32/uint32 arrays must be 4-byte aligned");
+  return hip_status(sv::launch_build_mask(attn_parent, sp_flag, n_q, B, Tq, mask_bits, sp_bits,
+                                          static_cast<hipStream_t>(stream)),
+                    "spec_build_mask launch");
+}
+
+size_t spec_verify_attn_workspace(const spec_attn_desc* d) {
+  if (check_desc(d) != SPEC_OK) return 0;
+  return sv::plan_attn(*d).ws_bytes;
+}
+
+int spec_verify_attn(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
+                     const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
+                     const int32_t* n_q, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const int st = check_desc(d);
+  if (st != SPEC_OK) return st;
+  if (d->B == 0) return ok();
+  REQUIRE(q && k_cache && v_cache && cache_len && k_blk && v_blk && mask_bits && n_q && out, SPEC_EINVAL,
+          "q, k_cache, v_cache, cache_len, k_blk, v_blk, mask_bits, n_q and out must be non-NULL");
+  if (d->S > 0) {
+    REQUIRE(k_soft && v_soft && sp_bits, SPEC_EINVAL, "S = %d needs k_soft, v_soft and sp_bits", d->S);
+  } else {
+    REQUIRE(!k_soft && !v_soft, SPEC_EINVAL, "k_soft / v_soft given with S = 0");
+  }
+  REQUIRE(aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(k_blk, 16) &&
+              aligned(v_blk, 16) && aligned(out, 16) && aligned(k_soft, 16) && aligned(v_soft, 16),
+          SPEC_EINVAL, "q, caches, block, soft and out must be 16-byte aligned");
+  REQUIRE(aligned(cache_len, 4) && aligned(mask_bits, 4) && aligned(sp_bits, 4) && aligned(n_q, 4) &&
+              aligned(lse, 4),
+          SPEC_EINVAL, "int32/uint32/float arrays must be 4-byte aligned");
+
+  const sv::AttnPlan plan = sv::plan_attn(*d);
+  if (plan.ws_bytes > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, SPEC_EWORKSPACE,
+            "workspace of %zu bytes needed, %zu given", plan.ws_bytes, workspace ? workspace_bytes : 0);
+    REQUIRE(aligned(workspace, 16), SPEC_EINVAL, "workspace must be 16-byte aligned");
+  }
+
+  sv::AttnArgs a{};
+  a.B = d->B;
+  a.Tq = d->Tq;
+  a.Hq = d->Hq;
+  a.Hkv = d->Hkv;
+  a.G = d->Hq / d->Hkv;
+  a.D = d->D;
+  a.S = d->S;
+  a.W = (d->Tq + 31) / 32;
+  a.R = a.G * d->Tq;
+  const float scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->D);
+  a.c = scale * 1.4426950408889634f;
+  a.lmax = d->lmax;
+  a.sb = d->kv_stride_b;
+  a.sl = d->kv_stride_l;
+  a.sh = d->kv_stride_h;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_len = cache_len;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.k_soft = k_soft;
+  a.v_soft = v_soft;
+  a.mask_bits = mask_bits;
+  a.sp_bits = sp_bits;
+  a.n_q = n_q;
+  a.out = out;
+  a.lse = lse;
+  a.n_split = plan.n_split;
+  a.row_chunks = plan.row_chunks;
+  a.rows_per_wg = plan.rows_per_wg;
+  if (plan.n_split > 1) {
+    const size_t rows = (size_t)plan.n_split * d->B * d->Hkv * a.R;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    const size_t off = (rows * d->D * sizeof(float) + 255) & ~size_t(255);
+    a.part_ml = reinterpret_cast<float*>(ws + off);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = plan.path == sv::PATH_MFMA ? sv::launch_attn_mfma(a, s) : sv::launch_attn_valu(a, d->dtype, s);
+  if (e != hipSuccess) return hip_status(e, "spec_verify_attn launch");
+  if (plan.n_split > 1) {
+    e = sv::launch_attn_combine(a, s);
+    if (e != hipSuccess) return hip_status(e, "spec_verify_attn combine launch");
+  }
+  return ok();
+}
+
+int spec_argmax_accept(const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,
+                       const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
+                       int32_t max_depth, int32_t* out_argmax, int32_t* out_len, int32_t* out_path,
+                       void* stream) {
+  REQUIRE(B >= 0, SPEC_EINVAL, "B = %d < 0", B);
+  REQUIRE(T >= 1 && T <= SPEC_MAX_NODES, SPEC_EINVAL, "T = %d outside [1, %d]", T, SPEC_MAX_NODES);
+  REQUIRE(V >= 1, SPEC_EINVAL, "V = %d < 1", V);
+  REQUIRE(max_depth >= 1 && max_depth <= SPEC_MAX_DEPTH, SPEC_EINVAL, "max_depth = %d outside [1, %d]",
+          max_depth, SPEC_MAX_DEPTH);
+  REQUIRE(logits_dtype == SPEC_F32 || logits_dtype == SPEC_BF16, SPEC_EINVAL,
+          "logits_dtype = %d is not a spec_dtype", logits_dtype);
+  REQUIRE((int64_t)B * T <= 0x7fffffff, SPEC_EUNSUPPORTED, "B * T too large");
+  if (B == 0) return ok();
+  REQUIRE(logits && n_nodes && draft_tok && acc_parent && out_argmax && out_len && out_path, SPEC_EINVAL,
+          "all array arguments must be non-NULL");
+  REQUIRE(aligned(logits, esize_of(logits_dtype)), SPEC_EINVAL, "logits must be aligned to its element size");
+  REQUIRE(aligned(n_nodes, 4) && aligned(draft_tok, 4) && aligned(acc_parent, 4) && aligned(out_argmax, 4) &&
+              aligned(out_len, 4) && aligned(out_path, 4),
+          SPEC_EINVAL, "int32 arrays must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = sv::launch_argmax(logits, logits_dtype, B, T, V, n_nodes, out_argmax, s);
+  if (e != hipSuccess) return hip_status(e, "spec_argmax_accept argmax launch");
+  e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, out_argmax, max_depth, out_len, out_path, s);
+  return hip_status(e, "spec_argmax_accept scan launch");
+}
+
+int spec_commit_kv(const spec_attn_desc* d, void* k_cache, void* v_cache, const int32_t* cache_len_in,
+                   int32_t* cache_len_out, const void* k_blk, const void* v_blk, const int32_t* out_len,
+                   const int32_t* out_path, int32_t max_depth, void* stream) {
+  const int st = check_desc(d);
+  if (st != SPEC_OK) return st;
+  REQUIRE(max_depth >= 1 && max_depth <= SPEC_MAX_DEPTH, SPEC_EINVAL, "max_depth = %d outside [1, %d]",
+          max_depth, SPEC_MAX_DEPTH);
+  if (d->B == 0) return ok();
+  REQUIRE(k_cache && v_cache && cache_len_in && cache_len_out && k_blk && v_blk && out_len && out_path,
+          SPEC_EINVAL, "all array arguments must be non-NULL");
+  REQUIRE(aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(k_blk, 16) && aligned(v_blk, 16),
+          SPEC_EINVAL, "caches and block must be 16-byte aligned");
+  REQUIRE(aligned(cache_len_in, 4) && aligned(cache_len_out, 4) && aligned(out_len, 4) && aligned(out_path, 4),
+          SPEC_EINVAL, "int32 arrays must be 4-byte aligned");
+  const hipError_t e =
+      sv::launch_commit(d->B, d->Tq, d->Hkv, d->D, esize_of(d->dtype), d->lmax, d->kv_stride_b,
+                        d->kv_stride_l, d->kv_stride_h, k_cache, v_cache, cache_len_in, cache_len_out, k_blk,
+                        v_blk, out_len, out_path, max_depth, static_cast<hipStream_t>(stream));
+  return hip_status(e, "spec_commit_kv launch");
+}
+
+}  // extern "C"

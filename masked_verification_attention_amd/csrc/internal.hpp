@@ -1,0 +1,71 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel
+// translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+// Fully resolved arguments of one verify-attention call.
+struct AttnArgs {
+  int B, Tq, Hq, Hkv, G, D, S, W;   // W = mask words per row
+  int R;                            // attention rows per (request, kv-head) = G * Tq
+  float c;                          // softmax scale * log2(e): scores live in the log2 domain
+  int64_t lmax, sb, sl, sh;         // cache capacity and element strides
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cache_len;
+  const void* k_blk;
+  const void* v_blk;
+  const void* k_soft;
+  const void* v_soft;
+  const uint32_t* mask_bits;
+  const uint32_t* sp_bits;
+  const int32_t* n_q;
+  float* out;
+  float* lse;
+  // split-KV partials (only when n_split > 1):
+  //   part_o  [n_split][B][Hkv][R][D]  unnormalised accumulators
+  //   part_ml [n_split][B][Hkv][R][2]  running max (log2 domain) and sum
+  float* part_o;
+  float* part_ml;
+  int n_split;
+  int row_chunks;                   // MFMA path: row chunks per (request, kv-head)
+  int rows_per_wg;                  // MFMA path: 64 or 128 rows per workgroup
+};
+
+enum AttnPath { PATH_VALU = 0, PATH_MFMA = 1 };
+
+struct AttnPlan {
+  AttnPath path;
+  int n_split;
+  int row_chunks;
+  int rows_per_wg;
+  size_t ws_bytes;
+};
+
+// Schedule for a validated descriptor (deterministic in the descriptor).
+AttnPlan plan_attn(const spec_attn_desc& d);
+
+hipError_t launch_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag, const int32_t* n_q,
+                             int B, int Tq, uint32_t* mask_bits, uint32_t* sp_bits, hipStream_t st);
+hipError_t launch_attn_valu(const AttnArgs& a, int dtype, hipStream_t st);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);
+hipError_t launch_argmax(const void* logits, int dtype, int B, int T, int V, const int32_t* n_nodes,
+                         int32_t* out_argmax, hipStream_t st);
+hipError_t launch_accept(int B, int T, const int32_t* n_nodes, const int32_t* draft_tok,
+                         const int32_t* acc_parent, const int32_t* argmax, int max_depth,
+                         int32_t* out_len, int32_t* out_path, hipStream_t st);
+hipError_t launch_commit(int B, int Tq, int Hkv, int D, int esize, int64_t lmax, int64_t sb,
+                         int64_t sl, int64_t sh, void* k_cache, void* v_cache,
+                         const int32_t* cache_len_in, int32_t* cache_len_out, const void* k_blk,
+                         const void* v_blk, const int32_t* out_len, const int32_t* out_path,
+                         int max_depth, hipStream_t st);
+
+}  // namespace sv

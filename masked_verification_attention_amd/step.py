@@ -1,0 +1,119 @@
+"""Device buffers for one verification step and the calls that run it.
+
+Uploads one seeded workload (``workloads.generate``) to HBM as torch tensors,
+allocates every output, and runs the four entry points on one stream:
+spec_build_mask -> spec_verify_attn -> spec_argmax_accept -> spec_commit_kv.
+This module only moves memory and marshals arguments; all arithmetic runs in
+the HIP kernels.  torch supplies the device memory and the stream.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import binding as bd
+from .workloads import VerifyConfig
+
+DTYPE_CODE = {"f32": bd.SPEC_F32, "bf16": bd.SPEC_BF16}
+
+
+def to_device(x: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Upload a generator array; bf16 arrays arrive as uint16 bit patterns."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    if dtype == "i32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(device)
+    if dtype == "u8":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(device)
+    raise ValueError(dtype)
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy with the exact bits (bf16 as uint16, int32 words as uint32)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class VerifyStep:
+    """One verification step's device state for a workload."""
+
+    def __init__(self, cfg: VerifyConfig, x: Dict[str, np.ndarray], device="cuda", kv_splits: int = 0,
+                 scale: float = 0.0, max_depth: Optional[int] = None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        dt = cfg.dtype
+        dev = self.device
+        self.B, self.Tq = x["q"].shape[0], x["q"].shape[1]
+        self.T = x["acc_parent"].shape[1]
+        self.W = (self.Tq + 31) // 32
+        self.lmax = x["k_cache"].shape[1]
+        self.max_depth = int(max_depth if max_depth is not None else min(cfg.max_depth, bd.SPEC_MAX_DEPTH))
+        self.q = to_device(x["q"], dt, dev)
+        self.k_cache = to_device(x["k_cache"], dt, dev)
+        self.v_cache = to_device(x["v_cache"], dt, dev)
+        self.k_blk = to_device(x["k_blk"], dt, dev)
+        self.v_blk = to_device(x["v_blk"], dt, dev)
+        self.k_soft = to_device(x["k_soft"], dt, dev) if cfg.S else None
+        self.v_soft = to_device(x["v_soft"], dt, dev) if cfg.S else None
+        self.cache_len = to_device(x["cache_len"], "i32", dev)
+        self.attn_parent = to_device(x["attn_parent"], "i32", dev)
+        self.sp_flag = to_device(x["sp_flag"], "u8", dev)
+        self.n_q = to_device(x["n_q"], "i32", dev)
+        self.acc_parent = to_device(x["acc_parent"], "i32", dev)
+        self.n_nodes = to_device(x["n_nodes"], "i32", dev)
+        self.draft_tok = to_device(x["draft_tok"], "i32", dev) if "draft_tok" in x else None
+        self.logits = to_device(x["logits"], cfg.logits_dtype, dev) if "logits" in x else None
+        self.V = x["logits"].shape[2] if "logits" in x else cfg.V
+
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.mask_bits = torch.zeros(self.B, self.Tq, self.W, **i32)
+        self.sp_bits = torch.zeros(self.B, self.W, **i32)
+        self.out = torch.empty(self.B, self.Tq, cfg.Hq, cfg.D, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(self.B, self.Tq, cfg.Hq, dtype=torch.float32, device=dev)
+        self.argmax = torch.empty(self.B, self.T, **i32)
+        self.out_len = torch.empty(self.B, **i32)
+        self.out_path = torch.empty(self.B, self.max_depth, **i32)
+        self.cache_len_out = torch.empty(self.B, **i32)
+
+        Hkv, D = cfg.Hkv, cfg.D
+        self.desc = bd.make_desc(self.B, self.Tq, cfg.Hq, Hkv, D, cfg.S, DTYPE_CODE[dt], self.lmax,
+                                 (self.lmax * Hkv * D, Hkv * D, D), scale=scale, kv_splits=kv_splits)
+        self.ws_bytes = bd.spec_verify_attn_workspace(self.desc)
+        self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+                          if self.ws_bytes else None)
+
+    # -- the four entry points
+    def build_mask(self, stream=None):
+        bd.spec_build_mask(self.attn_parent, self.sp_flag, self.n_q, self.B, self.Tq, self.mask_bits,
+                           self.sp_bits, stream)
+
+    def attention(self, stream=None, out=None, lse="self"):
+        bd.spec_verify_attn(self.desc, self.q, self.k_cache, self.v_cache, self.cache_len, self.k_blk,
+                            self.v_blk, self.k_soft, self.v_soft, self.mask_bits,
+                            self.sp_bits if self.cfg.S else self.sp_bits, self.n_q,
+                            self.out if out is None else out, self.lse if lse == "self" else lse,
+                            self.workspace, self.ws_bytes, stream)
+
+    def argmax_accept(self, stream=None):
+        bd.spec_argmax_accept(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.T, self.V,
+                              self.n_nodes, self.draft_tok, self.acc_parent, self.max_depth, self.argmax,
+                              self.out_len, self.out_path, stream)
+
+    def commit(self, stream=None, in_place=False):
+        bd.spec_commit_kv(self.desc, self.k_cache, self.v_cache, self.cache_len,
+                          self.cache_len if in_place else self.cache_len_out, self.k_blk, self.v_blk,
+                          self.out_len, self.out_path, self.max_depth, stream)
+
+    def run(self, stream=None):
+        """One pass of the whole hot path (the cache length is not advanced in place)."""
+        self.build_mask(stream)
+        self.attention(stream)
+        self.argmax_accept(stream)
+        self.commit(stream)

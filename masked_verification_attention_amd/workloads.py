@@ -132,8 +132,9 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Inputs must be finite (the draws are).  This is a storage conversion of the
     synthetic draws, not part of the verification arithmetic.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite floats are below 0x7F800000 in magnitude bits, so the sum cannot wrap
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 

@@ -1,0 +1,137 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from masked_verification_attention_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(bd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_version():
+    assert bd.spec_strerror(0) == "success"
+    assert bd.spec_strerror(bd.SPEC_EWORKSPACE).startswith("workspace")
+    assert bd.spec_strerror(12345) == "unknown status"
+    assert re.match(r"\d+\.\d+\.\d+$", bd.spec_version())
+
+
+def good_desc(**kw):
+    d = dict(B=2, Tq=60, Hq=32, Hkv=8, D=128, S=16, dtype=bd.SPEC_BF16, lmax=4156,
+             strides=(4156 * 8 * 128, 8 * 128, 128))
+    d.update(kw)
+    return bd.make_desc(d["B"], d["Tq"], d["Hq"], d["Hkv"], d["D"], d["S"], d["dtype"], d["lmax"],
+                        d["strides"], scale=d.get("scale", 0.0), kv_splits=d.get("kv_splits", 0))
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-NULL address that is never dereferenced on this path
+
+
+def attn(desc, **over):
+    args = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, cache_len=FAKE, k_blk=FAKE, v_blk=FAKE,
+                k_soft=FAKE if desc.S else None, v_soft=FAKE if desc.S else None, mask_bits=FAKE,
+                sp_bits=FAKE, n_q=FAKE, out=FAKE, lse=None, workspace=None, workspace_bytes=0)
+    args.update(over)
+    bd.spec_verify_attn(desc, args["q"], args["k_cache"], args["v_cache"], args["cache_len"], args["k_blk"],
+                        args["v_blk"], args["k_soft"], args["v_soft"], args["mask_bits"], args["sp_bits"],
+                        args["n_q"], args["out"], args["lse"], args["workspace"], args["workspace_bytes"],
+                        stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Tq=0), bd.SPEC_EINVAL), (dict(Tq=257), bd.SPEC_EINVAL), (dict(B=-1), bd.SPEC_EINVAL),
+    (dict(Hq=30), bd.SPEC_EINVAL), (dict(Hkv=0), bd.SPEC_EINVAL), (dict(D=96), bd.SPEC_EUNSUPPORTED),
+    (dict(S=-1), bd.SPEC_EINVAL), (dict(S=257), bd.SPEC_EINVAL), (dict(dtype=7), bd.SPEC_EINVAL),
+    (dict(lmax=-5), bd.SPEC_EINVAL), (dict(strides=(0, 1024, 128)), bd.SPEC_EINVAL),
+    (dict(strides=(4156 * 1024, 1028, 128)), bd.SPEC_EINVAL), (dict(scale=float("nan")), bd.SPEC_EINVAL),
+    (dict(scale=-1.0), bd.SPEC_EINVAL), (dict(kv_splits=65), bd.SPEC_EINVAL),
+    (dict(B=9000), bd.SPEC_EUNSUPPORTED),
+])
+def test_verify_attn_rejects_bad_descriptor(kw, status):
+    d = good_desc(**kw)
+    with pytest.raises(bd.SpecError) as e:
+        attn(d)
+    assert e.value.status == status
+    assert bd.spec_last_error() != ""
+    assert bd.spec_verify_attn_workspace(d) == 0
+
+
+def test_verify_attn_rejects_bad_pointers_and_workspace():
+    d = good_desc()
+    for name in ("q", "k_cache", "cache_len", "mask_bits", "n_q", "out"):
+        with pytest.raises(bd.SpecError) as e:
+            attn(d, **{name: None})
+        assert e.value.status == bd.SPEC_EINVAL
+    with pytest.raises(bd.SpecError) as e:       # soft prompt missing although S > 0
+        attn(d, k_soft=None)
+    assert e.value.status == bd.SPEC_EINVAL
+    with pytest.raises(bd.SpecError) as e:       # soft prompt given with S == 0
+        attn(good_desc(S=0), k_soft=FAKE, v_soft=FAKE)
+    assert e.value.status == bd.SPEC_EINVAL
+    with pytest.raises(bd.SpecError) as e:       # misaligned
+        attn(d, q=FAKE + 2)
+    assert e.value.status == bd.SPEC_EINVAL
+    dsplit = good_desc(kv_splits=4)
+    need = bd.spec_verify_attn_workspace(dsplit)
+    assert need > 0
+    with pytest.raises(bd.SpecError) as e:
+        attn(dsplit, workspace=FAKE, workspace_bytes=need - 1)
+    assert e.value.status == bd.SPEC_EWORKSPACE
+    with pytest.raises(bd.SpecError) as e:
+        attn(dsplit, workspace=None, workspace_bytes=need)
+    assert e.value.status == bd.SPEC_EWORKSPACE
+
+
+def test_empty_batch_is_a_noop_without_touching_memory():
+    attn(good_desc(B=0), q=None, out=None)
+    bd.spec_build_mask(None, None, None, 0, 8, None, None, stream=0)
+    bd.spec_argmax_accept(None, bd.SPEC_BF16, 0, 4, 100, None, None, None, 4, None, None, None, stream=0)
+    bd.spec_commit_kv(good_desc(B=0), None, None, None, None, None, None, None, None, 4, stream=0)
+
+
+def test_other_entry_points_reject_bad_arguments():
+    cases = [
+        lambda: bd.spec_build_mask(FAKE, None, FAKE, 2, 0, FAKE, FAKE, stream=0),
+        lambda: bd.spec_build_mask(FAKE, None, FAKE, 2, 300, FAKE, FAKE, stream=0),
+        lambda: bd.spec_build_mask(None, None, FAKE, 2, 8, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 0, 100, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 4, 0, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, 17, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept(FAKE, 3, 2, 4, 100, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, None, FAKE, 4, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_commit_kv(good_desc(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0),
+        lambda: bd.spec_commit_kv(good_desc(), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, stream=0),
+        lambda: bd.spec_commit_kv(good_desc(D=80), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, stream=0),
+    ]
+    for f in cases:
+        with pytest.raises(bd.SpecError):
+            f()
+
+
+def test_workspace_policy():
+    # the tree/contemplate shape fills the chip without splitting; lookahead rows split ragged prefixes
+    assert bd.spec_verify_attn_workspace(good_desc(B=16)) == 0
+    la = good_desc(B=8, Tq=8, Hq=32, Hkv=32, S=0, lmax=2056, strides=(2056 * 32 * 128, 32 * 128, 128))
+    assert bd.spec_verify_attn_workspace(la) > 0
