@@ -1,0 +1,210 @@
+"""Benchmark of the verification step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of the ConFu-shaped
+Llama-3-8B workload (16 requests, 32 query / 8 kv heads, head dim 128, bf16,
+4096-token prefix + 16 soft-prompt rows, 30-node draft tree + 30 contemplate
+rows = 60 query rows per request, 128256-entry vocabulary):
+    spec_build_mask -> spec_verify_attn -> spec_argmax_accept -> spec_commit_kv
+Inputs are resident in HBM before timing starts; three independent input
+sets (~1.3 GB) are cycled so that the 256 MB last-level cache cannot hold a
+step's working set.  The metric is speculative query tokens verified per
+second (sum of valid block rows / step time).
+
+Printed: one JSON line on stdout; details on stderr.  The roofline object
+describes the attention kernel (the dominant one): algorithmic bytes per
+launch / its mean duration, timed with HIP events on the launch stream.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+WORKLOAD = "c3_confu_8b"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_mfma_c3_counters.json")
+ATTN_SRC = os.path.join(ROOT, "masked_verification_attention_amd", "csrc", "attn_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_algorithmic_bytes(cfg, x) -> int:
+    """Bytes the attention must move at least once: KV prefix read, soft prompt,
+    queries, block K/V, mask words and the fp32 output (+ lse)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    B, Tq = x["q"].shape[:2]
+    W = (Tq + 31) // 32
+    kv = int(x["cache_len"].astype(np.int64).sum()) * cfg.Hkv * cfg.D * 2 * es
+    soft = cfg.S * cfg.Hkv * cfg.D * 2 * es
+    q = B * Tq * cfg.Hq * cfg.D * es
+    blk = B * Tq * cfg.Hkv * cfg.D * 2 * es
+    mask = B * Tq * W * 4 + B * W * 4
+    out = B * Tq * cfg.Hq * cfg.D * 4 + B * Tq * cfg.Hq * 4
+    return kv + soft + q + blk + mask + out
+
+
+def attention_flops(cfg, x) -> int:
+    """4*D flops per visible (query head, key) pair; visible pairs counted from the inputs."""
+    B, Tq = x["q"].shape[:2]
+    total = 0
+    for b in range(B):
+        L = int(x["cache_len"][b])
+        nq = int(x["n_q"][b])
+        for r in range(nq):
+            depth = 1
+            p = int(x["attn_parent"][b, r])
+            while p >= 0:
+                depth += 1
+                p = int(x["attn_parent"][b, p])
+            soft = cfg.S if x["sp_flag"][b, r] else 0
+            total += (L + soft + depth) * cfg.Hq
+    return total * 4 * cfg.D
+
+
+def counters_traffic():
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, or None
+    if the kernel source changed since they were taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if rec.get("kernel_src_sha256") != sha:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(requests: int):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from masked_verification_attention_amd import workloads as wl
+
+    cfg = wl.CONFIGS[WORKLOAD]
+    x = wl.generate(cfg, B=requests)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.build_mask(x["attn_parent"], x["sp_flag"], x["n_q"])
+        oracle.verify_attention(x["q"], x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"],
+                                x["k_soft"], x["v_soft"], x["attn_parent"], x["sp_flag"], x["n_q"], cfg.dtype)
+        _, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                          x["acc_parent"], cfg.max_depth)
+        oracle.commit_kv(x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"], A, path)
+        dt = time.perf_counter() - t0
+    tokens = int(x["n_q"].sum())
+    return {"value": tokens / dt, "unit": "spec query tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{requests} of the 16 requests of the workload ({tokens} query tokens, full "
+                      f"4096-token prefix), whole step (mask, attention, argmax+acceptance, commit), "
+                      f"fp64 numpy, BLAS limited to 1 thread; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="input sets cycled between steps")
+    ap.add_argument("--cpu-requests", type=int, default=6, help="requests in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-splits", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from masked_verification_attention_amd import workloads as wl
+    from masked_verification_attention_amd.step import VerifyStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = wl.CONFIGS[WORKLOAD]
+    steps_state = []
+    t0 = time.time()
+    for i in range(args.sets):
+        x = wl.generate(cfg, seed=cfg.seed + 100 * i)
+        st = VerifyStep(cfg, x, device="cuda:0", kv_splits=args.kv_splits)
+        steps_state.append((st, x))
+    torch.cuda.synchronize()
+    log(f"inputs: {args.sets} sets generated and uploaded in {time.time() - t0:.1f}s")
+    x0 = steps_state[0][1]
+    tokens_per_step = int(x0["n_q"].sum())
+    alg_bytes = attention_algorithmic_bytes(cfg, x0)
+    flops = attention_flops(cfg, x0)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        steps_state[i % args.sets][0].run(stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        st = steps_state[i % args.sets][0]
+        st.build_mask(stream)
+        ev[i][0].record(stream)
+        st.attention(stream)
+        ev[i][1].record(stream)
+        st.argmax_accept(stream)
+        st.commit(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    attn_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    attn_mean = float(attn_us.mean())
+    ms_per_step = elapsed * 1e3 / K
+    value = tokens_per_step * K / elapsed
+    achieved = alg_bytes / (attn_mean * 1e-6) / 1e9
+    tflops = flops / (attn_mean * 1e-6) / 1e12
+    log(f"step {ms_per_step * 1e3:.1f} us; attention mean {attn_mean:.1f} us (p10 {np.percentile(attn_us, 10):.1f}, "
+        f"p90 {np.percentile(attn_us, 90):.1f}); {alg_bytes / 1e6:.1f} MB -> {achieved:.0f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of HBM peak); {flops / 1e9:.1f} GFLOP -> {tflops:.0f} TFLOP/s "
+        f"({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of bf16 MFMA peak); ws {steps_state[0][0].ws_bytes} B")
+
+    result = {
+        "metric": "verify-attn spec query tokens/s + achieved HBM GB/s (% of peak), 1 MI355X",
+        "value": value,
+        "unit": "spec query tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "ConFu-shaped Llama-3-8B verify: batch 16, 32q/8kv heads, head_dim 128, "
+                               "prefix 4096 + 16 soft rows, 30-node tree + 30 contemplate rows, vocab 128256",
+                   "global_batch": cfg.B, "seq_len": 4096, "query_rows": cfg.Tq, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counters_traffic(),
+                     "kernel": "k_attn_mfma", "algorithmic_bytes_per_launch": alg_bytes,
+                     "mean_launch_us": attn_mean, "tflops": tflops},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_requests)
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s ({result['cpu_baseline']['sample']})")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,6 +60,8 @@ int check_desc(const spec_attn_desc* d) {
   REQUIRE((d->kv_stride_b * es) % 16 == 0 && (d->kv_stride_l * es) % 16 == 0 && (d->kv_stride_h * es) % 16 == 0,
           SPEC_EINVAL, "cache strides must be multiples of 16 bytes");
   REQUIRE(d->kv_stride_h >= d->D || d->Hkv == 1, SPEC_EINVAL, "kv_stride_h < D would overlap heads");
+  REQUIRE(d->kv_stride_l * es <= (int64_t(1) << 25), SPEC_EUNSUPPORTED,
+          "kv_stride_l of %lld elements exceeds 32 MiB per cache row", (long long)d->kv_stride_l);
   REQUIRE(d->kv_splits >= 0 && d->kv_splits <= 64, SPEC_EINVAL, "kv_splits = %d outside [0, 64]", d->kv_splits);
   REQUIRE(d->reserved == 0, SPEC_EINVAL, "reserved field must be 0");
   REQUIRE(isfinite(d->scale) && d->scale >= 0.f, SPEC_EINVAL, "scale must be finite and >= 0 (0 = 1/sqrt(D))");

@@ -10,40 +10,67 @@
 // keys whose mask bit is set.  Online softmax in the log2 domain, fp32
 // accumulation, probabilities rounded to bf16 for the P*V product.
 //
-// Layout of the work.  Rows of one (request, kv-head) are m = r * G + g
-// (block row r, head g of the group), so the G heads of one block row are
-// adjacent and share its mask word.  A workgroup of 4 waves owns 64 * NB
-// rows; wave w owns NB blocks of 16 rows.  Keys stream in 32-key tiles that
-// the whole workgroup stages in LDS (double-buffered, one barrier per tile):
-//   K tile row-major [key][d]  -> A operand of S^T = K Q^T
-//   V tile transposed [d][key] -> A operand of O^T = V^T P^T
-// With S^T and O^T every lane holds one query row (lane % 16) for all its
-// values: the row's 8 scores of a tile become the B operand of the P*V MFMA
-// directly (the contraction order over keys is permuted identically in V^T),
-// and the row's running max / scale apply to its own O^T values.  Only the
-// max needs a cross-lane step (the row's 32 keys sit in 4 lanes).
+// Work layout
+//   Rows of one (request, kv-head) are m = r * G + g (block row r, head g of
+//   the group), so the G heads of a block row are adjacent and share its mask
+//   word.  A workgroup owns 64 * NB rows and has 8 waves in two groups of 4;
+//   wave w of a group owns NB blocks of 16 rows.  The two groups take
+//   alternate 32-key tiles of the same key stream (a split of the keys inside
+//   the workgroup) and merge their softmax states through LDS at the end, so
+//   every SIMD runs two waves whose matrix and vector phases interleave.
 //
-// Key list of a workgroup: prefix keys [ks, ke) of its split, then -- for
-// the last split only -- the S soft keys and the block rows.  Segments are
-// tiled separately, so prefix tiles carry no mask (only the ragged tail is
-// cut); soft and block tiles test the sp bit and the row's mask word.
+// Key stream
+//   Keys are the prefix range of this split, then -- last split only -- the S
+//   soft keys and the block rows.  Segments are tiled separately, so prefix
+//   tiles need no mask except the ragged tail.  Tiles are copied straight from
+//   HBM into a ring of LDS slots with 16-byte direct-to-LDS loads, four tiles
+//   ahead of the compute, one barrier per pair of tiles.  Each wave is
+//   software-pipelined: the scores of its tile t are computed while the P*V
+//   product of its tile t-1 runs, so matrix and vector work overlap.  K and V sit
+//   row-major in a slot with the 16-byte chunks of key row k stored at chunk
+//   position (c ^ k mod 16), which keeps both read patterns below free of bank
+//   conflicts:
+//     S^T = K Q^T : K is the A operand, one 16-byte read per lane;
+//     O^T = V^T P^T : V^T is the A operand, built by the transposing 64-bit
+//                     LDS read (lane j of a 16-lane group receives element
+//                     j % 4 of the 8 bytes addressed by lane 4e + j / 4 of its
+//                     group, for e = 0..3).
+//   With S^T and O^T every lane holds one query row (lane % 16) for all its
+//   values: the row's 8 scores of a tile become the P operand directly (the
+//   contraction order over keys is permuted the same way in V^T), and the
+//   row's max and scale apply to its own O^T values.
+//
+// Softmax: the running max only moves when a tile's max exceeds it by more
+// than 8 (in log2 units), so after the first tile rows are almost never
+// rescaled; probabilities stay below 2^8, far from fp32 / bf16 limits.  The
+// common path does not even compute the tile max: the probabilities against
+// the current max are needed anyway, and their sum exceeds 2^8 whenever one of
+// them could.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
 namespace sv {
 
-constexpr int kMfmaThreads = 256;
-constexpr int kTileK = 32;
-
-template <int D>
-struct MfmaLds {
-  static constexpr int kKStride = D * 2 + 16;        // bytes per K row (padded)
-  static constexpr int kVtStride = kTileK * 2 + 4;   // bytes per transposed V row (one head dim)
-  static constexpr int kKBytes = kTileK * kKStride;
-  static constexpr int kVtBytes = D * kVtStride;
-  static constexpr int kBufBytes = kKBytes + kVtBytes;
-  static constexpr int kChunks = kTileK * D / 8;     // 16-byte chunks per K (or V) tile
-  static constexpr int kChunksPerThread = (kChunks + kMfmaThreads - 1) / kMfmaThreads;
+template <int D, int NB>
+struct MfmaCfg {
+  static constexpr int kThreads = 512;
+  static constexpr int kWaves = 8;
+  static constexpr int TK = 32;                  // keys per tile
+  static constexpr int CH = D / 8;               // 16-byte chunks per key row
+  static constexpr int ROWB = D * 2;             // bytes per key row
+  static constexpr int TILEB = TK * ROWB;        // bytes of a K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;       // K + V
+  static constexpr int RPI = 64 / CH;            // key rows per 1 KB wave load
+  static constexpr int IPT = 2 * TK / RPI;       // wave loads per tile (K and V)
+  static constexpr int LPW = IPT / kWaves;       // wave loads per wave per tile
+  static constexpr int P = 4;                    // tiles in flight
+  static constexpr int NS = P + 4;               // ring slots: 2 scored + 2 awaiting P*V + P in flight
+  static constexpr bool kIssueLate = false;      // issue a step's loads after its compute
+  static constexpr int ROWS = 64 * NB;           // rows per workgroup
+  static constexpr int MAXW = (SPEC_MAX_TQ + 31) / 32;
+  static_assert(LPW >= 1 && IPT % kWaves == 0, "tile loads must split evenly over the waves");
 };
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -56,21 +83,61 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return r;
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+__device__ __forceinline__ lds_char* to_lds(const char* p) { return (lds_char*)(char*)p; }
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] and [15:14]; expcnt [6:4] and lgkmcnt [11:8] left unconstrained
+  constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+  __builtin_amdgcn_s_waitcnt(imm);
+}
+
+// 16-byte direct-to-LDS load: lane i's 16 bytes from src land at LDS byte
+// address lds + 16 i.  Issued through asm so that the compiler does not
+// serialise the ring with its own conservative waits; completion is tracked
+// explicitly with wait_vmcnt.  m0 is named as clobbered; the compiler reserves
+// m0 and warns that it does not preserve it across the asm, which is what is
+// wanted (this file is built with -Wno-inline-asm for that warning).
+__device__ __forceinline__ void dma16(uint32_t lds, const char* src) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D, int NB>
-__global__ __launch_bounds__(kMfmaThreads) void k_attn_mfma(AttnArgs a) {
-  using Lds = MfmaLds<D>;
+__global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
+  using C = MfmaCfg<D, NB>;
   constexpr int DC = D / 32;   // k-chunks of S^T = K Q^T
   constexpr int DB = D / 16;   // 16-wide head-dim blocks of O^T
-  constexpr int CPT = Lds::kChunksPerThread;
-  __shared__ __attribute__((aligned(16))) char lds[2 * Lds::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) char ring[C::NS * C::STAGEB];
+  __shared__ uint32_t mask_lds[C::ROWS][C::MAXW];
 
-  const int split = blockIdx.x;
-  const int chunk_id = blockIdx.y;
-  const int bh = blockIdx.z;
+  // ---- which (split, request, kv-head, row chunk): siblings of a row chunk
+  // sit on the same XCD (workgroups are dealt round-robin over 8 XCDs)
+  const int nwg = gridDim.x;
+  const int bid = blockIdx.x;
+  const int item = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+  const int chunk_id = item % a.row_chunks;
+  const int rest = item / a.row_chunks;
+  const int bh = rest % (a.B * a.Hkv);
+  const int split = rest / (a.B * a.Hkv);
   const int b = bh / a.Hkv;
   const int h = bh % a.Hkv;
+
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = wave >> 2;          // key-tile parity this wave computes
+  const int wq = wave & 3;            // row slice within the workgroup
   const int lane = tid % kWave;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
@@ -81,19 +148,26 @@ __global__ __launch_bounds__(kMfmaThreads) void k_attn_mfma(AttnArgs a) {
   const int ks = min(L, split * keys_per_split);
   const int ke = min(L, ks + keys_per_split);
   const bool last = split == a.n_split - 1;
-  const int ntp = (ke - ks + kTileK - 1) / kTileK;
-  const int nts = last ? (a.S + kTileK - 1) / kTileK : 0;
-  const int ntb = last ? (nq + kTileK - 1) / kTileK : 0;
+  const int ntp = (ke - ks + C::TK - 1) / C::TK;
+  const int nts = last ? (a.S + C::TK - 1) / C::TK : 0;
+  const int ntb = last ? (nq + C::TK - 1) / C::TK : 0;
   const int nt = ntp + nts + ntb;
 
-  // ---- this lane's rows: block nb covers rows rowbase + 16 nb + (0..15)
-  const int rowbase = chunk_id * (64 * NB) + wave * (16 * NB);
-  int row_r[NB], row_j[NB];
+  // ---- rows: mask words of the workgroup's rows into LDS; this lane's rows
+  const int row0 = chunk_id * C::ROWS;
+  for (int i = tid; i < C::ROWS * a.W; i += C::kThreads) {
+    const int rl = i / a.W, w = i % a.W;
+    const int m = row0 + rl;
+    const int r = m / a.G;
+    mask_lds[rl][w] = (m < a.R && r < nq) ? a.mask_bits[((int64_t)b * a.Tq + r) * a.W + w] : 0u;
+  }
+  int row_r[NB], row_j[NB], row_l[NB];
   bool row_ok[NB], row_sp[NB];
   bf16x8 qf[NB][DC];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int m = rowbase + 16 * nb + l16;
+    row_l[nb] = wq * (16 * NB) + 16 * nb + l16;
+    const int m = row0 + row_l[nb];
     const int r = m / a.G, g = m % a.G;
     row_r[nb] = r;
     row_j[nb] = h * a.G + g;
@@ -109,192 +183,301 @@ __global__ __launch_bounds__(kMfmaThreads) void k_attn_mfma(AttnArgs a) {
     }
   }
 
-  // ---- tile loader: global -> registers -> LDS
+  // ---- direct-to-LDS tile loads
   const char* kc = static_cast<const char*>(a.k_cache) + ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
   const char* vc = static_cast<const char*>(a.v_cache) + ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
-  const char* ksoft = static_cast<const char*>(a.k_soft);
-  const char* vsoft = static_cast<const char*>(a.v_soft);
   const char* kblk = static_cast<const char*>(a.k_blk) + ((int64_t)b * a.Tq * a.Hkv + h) * D * 2;
   const char* vblk = static_cast<const char*>(a.v_blk) + ((int64_t)b * a.Tq * a.Hkv + h) * D * 2;
-
-  u32x4 kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int ti) {
+  const char* ksoft = static_cast<const char*>(a.k_soft) + (int64_t)h * D * 2;
+  const char* vsoft = static_cast<const char*>(a.v_soft) + (int64_t)h * D * 2;
+  const int lrow = lane / C::CH;          // key row within the wave's 1 KB load
+  const int lpos = lane % C::CH;          // chunk position the lane fills
+  // per-tile source of its key rows (uniform); rows past the segment end are
+  // clamped to its last key and masked out in the compute
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_char*)ring;
+  int lane_row[C::LPW], lane_off[C::LPW];   // per load: key row in the tile, byte offset of its chunk
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + u * kMfmaThreads;
-      const int kk = c / (D / 8);
-      const int d0 = 8 * (c % (D / 8));
-      kreg[u] = u32x4{0u, 0u, 0u, 0u};
-      vreg[u] = u32x4{0u, 0u, 0u, 0u};
-      if (c >= Lds::kChunks) continue;
-      if (ti < ntp) {
-        const int key = ks + ti * kTileK + kk;
-        if (key < ke) {
-          const int64_t off = ((int64_t)key * a.sl + d0) * 2;
-          kreg[u] = ldg16(kc + off);
-          vreg[u] = ldg16(vc + off);
-        }
-      } else if (ti < ntp + nts) {
-        const int key = (ti - ntp) * kTileK + kk;
-        if (key < a.S) {
-          const int64_t off = (((int64_t)key * a.Hkv + h) * D + d0) * 2;
-          kreg[u] = ldg16(ksoft + off);
-          vreg[u] = ldg16(vsoft + off);
-        }
-      } else {
-        const int key = (ti - ntp - nts) * kTileK + kk;
-        if (key < nq) {
-          const int64_t off = ((int64_t)key * a.Hkv * D + d0) * 2;
-          kreg[u] = ldg16(kblk + off);
-          vreg[u] = ldg16(vblk + off);
-        }
-      }
+  for (int j = 0; j < C::LPW; ++j) {
+    const int ii = (wave * C::LPW + j) % (C::IPT / 2);
+    lane_row[j] = ii * C::RPI + lrow;
+    lane_off[j] = (lpos ^ (lane_row[j] & (C::CH - 1))) * 16;
+  }
+  auto issue_tile = [&](int t) {
+    const int ti = t < nt ? t : nt - 1;   // past the end: reload the last tile into an unused slot
+    const char* bk;
+    const char* bv;
+    int stride, nvalid;
+    if (ti < ntp) {
+      const int key0 = ks + ti * C::TK;
+      bk = kc + (int64_t)key0 * a.sl * 2;
+      bv = vc + (int64_t)key0 * a.sl * 2;
+      stride = (int)(a.sl * 2);
+      nvalid = ke - key0;
+    } else if (ti < ntp + nts) {
+      const int key0 = (ti - ntp) * C::TK;
+      bk = ksoft + (int64_t)key0 * a.Hkv * D * 2;
+      bv = vsoft + (int64_t)key0 * a.Hkv * D * 2;
+      stride = a.Hkv * D * 2;
+      nvalid = a.S - key0;
+    } else {
+      const int key0 = (ti - ntp - nts) * C::TK;
+      bk = kblk + (int64_t)key0 * a.Hkv * D * 2;
+      bv = vblk + (int64_t)key0 * a.Hkv * D * 2;
+      stride = a.Hkv * D * 2;
+      nvalid = nq - key0;
     }
-  };
-  auto store_tile = [&](int buf) {
-    char* kb = lds + buf * Lds::kBufBytes;
-    char* vt = kb + Lds::kKBytes;
+    const uint32_t slot = ring_lds + (t % C::NS) * C::STAGEB;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + u * kMfmaThreads;
-      if (c >= Lds::kChunks) continue;
-      const int kk = c / (D / 8);
-      const int d0 = 8 * (c % (D / 8));
-      *reinterpret_cast<u32x4*>(kb + kk * Lds::kKStride + d0 * 2) = kreg[u];
-      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t x = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
-        *reinterpret_cast<uint16_t*>(vt + (d0 + e) * Lds::kVtStride + kk * 2) = x;
-      }
+    for (int j = 0; j < C::LPW; ++j) {
+      const int ins = wave * C::LPW + j;             // 0 .. IPT-1
+      const bool is_v = ins >= C::IPT / 2;
+      const int ii = is_v ? ins - C::IPT / 2 : ins;
+      const int rel = min(lane_row[j], nvalid - 1);
+      const char* src = (is_v ? bv : bk) + (rel * stride + lane_off[j]);
+      dma16(slot + (is_v ? C::TILEB : 0) + ii * 1024, src);
     }
   };
 
-  float mrun[NB], lrun[NB];
+  float mrun[NB], lrun[NB], negm[NB];
   f32x4 o[NB][DB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    mrun[nb] = -INFINITY;
+    mrun[nb] = -INFINITY;   // running max, log2 units
+    negm[nb] = 0.f;         // -max used for the exponent (0 while no key is visible)
     lrun[nb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[nb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const int lx16 = ((lane ^ 16) << 2), lx32 = ((lane ^ 32) << 2);   // byte lane addresses for permutes
 
+  // setup loads (queries, flags, mask words) must land before the ring's vmcnt accounting starts
+  __builtin_amdgcn_s_waitcnt(0);
+  block_barrier();
+
+  const float P_LIMIT = 256.0f;   // 2^TAU with TAU = 8: bound on any probability between rescales
   if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int ti = 0; ti < nt; ++ti) {
-    const int buf = ti & 1;
-    if (ti + 1 < nt) load_tile(ti + 1);
-    const char* kb = lds + buf * Lds::kBufBytes;
-    const char* vt = kb + Lds::kKBytes;
-
-    // K fragments: key = 16 kb + l16, head dims 32 dc + 8 q4 .. +7
-    bf16x8 kf[2][DC];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        kf[kb2][dc] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(kb + (16 * kb2 + l16) * Lds::kKStride + (32 * dc + 8 * q4) * 2));
-
-    // segment of this tile and its masking rule (uniform over the workgroup)
-    const int seg = ti < ntp ? 0 : (ti < ntp + nts ? 1 : 2);
-    int lim = kTileK;                  // keys of the tile that exist
-    if (seg == 0) lim = min(kTileK, ke - (ks + ti * kTileK));
-    else if (seg == 1) lim = min(kTileK, a.S - (ti - ntp) * kTileK);
-    else lim = min(kTileK, nq - (ti - ntp - nts) * kTileK);
-
+    for (int t = 0; t < C::P; ++t) issue_tile(t);
+    const int nsteps = (nt + 1) / 2;
     bf16x8 pf[NB];
-    float alpha[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      f32x4 st[2];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) acc = mfma16x16x32(kf[kb2][dc], qf[nb][dc], acc);
-        st[kb2] = acc;
-      }
-      // visibility of the lane's 8 keys (tile keys 16 kb + 4 q4 + i) for its row
-      uint32_t vis = 0xffu;
-      if (seg == 0) {
-        if (lim < kTileK) {
-          vis = 0u;
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (16 * kb2 + 4 * q4 + i < lim) vis |= 1u << (4 * kb2 + i);
-        }
-        if (!row_ok[nb]) vis = 0u;
-      } else if (seg == 1) {
-        vis = 0u;
-        if (row_sp[nb]) {
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (16 * kb2 + 4 * q4 + i < lim) vis |= 1u << (4 * kb2 + i);
-        }
-      } else {
-        const int word = ti - ntp - nts;
-        const uint32_t mw =
-            row_ok[nb] ? a.mask_bits[((int64_t)b * a.Tq + row_r[nb]) * a.W + word] : 0u;
-        vis = 0u;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if ((mw >> (16 * kb2 + 4 * q4 + i)) & 1u) vis |= 1u << (4 * kb2 + i);
-      }
-      float x[8];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          x[4 * kb2 + i] = ((vis >> (4 * kb2 + i)) & 1u) ? st[kb2][i] * a.c : -INFINITY;
-      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[nb], mx);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      alpha[nb] = fast_exp2(mrun[nb] - muse);
-      mrun[nb] = mnew;
-      float p[8];
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(x[e] - muse);
-        ps += p[e];
-      }
-      lrun[nb] = lrun[nb] * alpha[nb] + ps;
-      const u32x4 packed = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-      pf[nb] = as_bf16x8(packed);
-    }
+    for (int nb = 0; nb < NB; ++nb) pf[nb] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    int tprev = -1;   // this wave's tile whose P*V is still to be done
 
-    // O^T += V^T P^T ; V^T fragment: head dim 16 db + l16, keys {4 q4 .. +3} and {16 + 4 q4 .. +3}
+    // step s: wait for tiles 2s, 2s+1, free the slots read two steps ago, refill
+    auto begin_step = [&](int s) {
+      wait_vmcnt<(C::P - 2) * C::LPW>();
+      block_barrier();
+      issue_tile(2 * s + C::P);
+      issue_tile(2 * s + C::P + 1);
+    };
+    // S^T = K Q^T for tile t
+    auto scores = [&](int t, f32x4 (&st)[NB][2]) {
+      const char* slotK = ring + (t % C::NS) * C::STAGEB;
+      // K fragments: key 16 kb + l16, head dims 32 dc + 8 q4 .. +7
+      bf16x8 kf[2][DC];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const char* vrow = vt + (16 * db + l16) * Lds::kVtStride + 8 * q4;
-      const u32x4 vv = {*reinterpret_cast<const uint32_t*>(vrow), *reinterpret_cast<const uint32_t*>(vrow + 4),
-                        *reinterpret_cast<const uint32_t*>(vrow + 32), *reinterpret_cast<const uint32_t*>(vrow + 36)};
-      const bf16x8 vf = as_bf16x8(vv);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 16 * kb + l16;
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          const int ch = (4 * dc + q4) ^ (row & (C::CH - 1));
+          kf[kb][dc] = as_bf16x8(*reinterpret_cast<const u32x4*>(slotK + row * C::ROWB + ch * 16));
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) acc = mfma16x16x32(kf[kb][dc], qf[nb][dc], acc);
+          st[nb][kb] = acc;
+        }
+    };
+    // O^T += V^T P^T for tile tp; V^T fragment for head dims 16 db + l16 and
+    // keys {4 q4 .. +3} (read 0) and {16 + 4 q4 .. +3} (read 1)
+    auto pv = [&](int tp) {
+      const char* slotV = ring + (tp % C::NS) * C::STAGEB + C::TILEB;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        uint32_t vw[4];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int row = 16 * cc + 4 * q4 + (l16 >> 2);
+          const int ch = (2 * db + ((l16 & 3) >> 1)) ^ (row & (C::CH - 1));
+          lds_char* p = to_lds(slotV) + row * C::ROWB + ch * 16 + 8 * (l16 & 1);
+          const bf16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+          uint32_t w2[2];
+          __builtin_memcpy(w2, &v4, 8);
+          vw[2 * cc] = w2[0];
+          vw[2 * cc + 1] = w2[1];
+        }
+        const bf16x8 vf = as_bf16x8(u32x4{vw[0], vw[1], vw[2], vw[3]});
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nb][db] = mfma16x16x32(vf, pf[nb], o[nb][db]);
+      }
+    };
+    auto pack = [&](int nb, const float (&p)[8]) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf16x2_t v2;
+        v2[0] = (__bf16)p[2 * e];
+        v2[1] = (__bf16)p[2 * e + 1];
+        pk[e] = __builtin_bit_cast(uint32_t, v2);
+      }
+      pf[nb] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+    };
+    // exact max of row block nb over xs, rescale its state, and recompute p
+    auto rescale = [&](int nb, const float (&xs)[8], float (&p)[8], float& ps) {
+      const float lmax = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])),
+                               fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
+      float mx = lmax * a.c;
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(lx16, __float_as_int(mx))));
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(lx32, __float_as_int(mx))));
+      const float mnew = fmaxf(mrun[nb], mx);
+      if (mnew != -INFINITY) {
+        const float alpha = (mrun[nb] == -INFINITY) ? 0.f : fast_exp2(mrun[nb] - mnew);
+        lrun[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[nb][db] *= alpha;
+        mrun[nb] = mnew;
+        negm[nb] = -mnew;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(xs[e], a.c, negm[nb]));
+      ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    };
+    // softmax of a complete prefix tile: no mask; probabilities against the current
+    // max, whose sum exceeds 2^TAU whenever one of them could (then rescale exactly)
+    auto softmax_full = [&](const f32x4 (&st)[NB][2], bool first) {
+      float xs[NB][8], p[NB][8], ps[NB];
+      bool need = first;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        f32x4 ov = o[nb][db];
-        ov *= alpha[nb];
-        o[nb][db] = mfma16x16x32(vf, pf[nb], ov);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xs[nb][e] = st[nb][e >> 2][e & 3];
+          p[nb][e] = fast_exp2(fmaf(xs[nb][e], a.c, negm[nb]));
+        }
+        ps[nb] = ((p[nb][0] + p[nb][1]) + (p[nb][2] + p[nb][3])) + ((p[nb][4] + p[nb][5]) + (p[nb][6] + p[nb][7]));
+        need = need || !(ps[nb] <= P_LIMIT);
       }
-    }
+      if (__any(need)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) rescale(nb, xs[nb], p[nb], ps[nb]);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        lrun[nb] += ps[nb];
+        pack(nb, p[nb]);
+      }
+    };
+    // softmax of a tile that needs masking: ragged prefix tail, soft prompt, block rows
+    auto softmax_masked = [&](int t, const f32x4 (&st)[NB][2], int seg, int lim) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        // visibility of the lane's 8 keys (tile keys 16 kb + 4 q4 + i) for its row
+        uint32_t vis;
+        if (seg == 0) {
+          vis = row_ok[nb] ? 0xffu : 0u;
+        } else if (seg == 1) {
+          vis = row_sp[nb] ? 0xffu : 0u;
+        } else {
+          const uint32_t mw = mask_lds[row_l[nb]][t - ntp - nts];
+          vis = ((mw >> (4 * q4)) & 0xfu) | (((mw >> (16 + 4 * q4)) & 0xfu) << 4);
+        }
+        uint32_t lm = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (((e < 4) ? 4 * q4 + e : 16 + 4 * q4 + e - 4) < lim) lm |= 1u << e;
+        vis &= lm;
+        float xs[8], p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xs[e] = ((vis >> e) & 1u) ? st[nb][e >> 2][e & 3] : -INFINITY;
+          p[e] = fast_exp2(fmaf(xs[e], a.c, negm[nb]));
+        }
+        float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        if (__any(!(ps <= P_LIMIT) || mrun[nb] == -INFINITY)) rescale(nb, xs, p, ps);
+        lrun[nb] += ps;
+        pack(nb, p);
+      }
+    };
+    // any step: the wave's tile may be missing, partial, soft or block
+    auto generic_step = [&](int s) {
+      begin_step(s);
+      const int t = 2 * s + grp;
+      const bool cur = (s < nsteps) && (t < nt);
+      f32x4 st[NB][2];
+      if (cur) scores(t, st);
+      if (tprev >= 0) pv(tprev);
+      if (cur) {
+        const int seg = t < ntp ? 0 : (t < ntp + nts ? 1 : 2);
+        int lim;
+        if (seg == 0) lim = min(C::TK, ke - (ks + t * C::TK));
+        else if (seg == 1) lim = min(C::TK, a.S - (t - ntp) * C::TK);
+        else lim = min(C::TK, nq - (t - ntp - nts) * C::TK);
+        if (seg == 0 && lim == C::TK) softmax_full(st, mrun[0] == -INFINITY || (NB > 1 && mrun[NB - 1] == -INFINITY));
+        else softmax_masked(t, st, seg, lim);
+        tprev = t;
+      } else {
+        tprev = -1;
+      }
+    };
 
-    if (ti + 1 < nt) store_tile(buf ^ 1);
-    __syncthreads();
+    // steps whose two tiles are complete prefix tiles, after the first, run the
+    // branch-free form: scores, the previous tile's P*V, softmax
+    const int nfull = (ke - ks) / C::TK;
+    const int s_hot_end = nfull / 2;
+    generic_step(0);
+    for (int s = 1; s < s_hot_end; ++s) {
+      begin_step(s);
+      const int t = 2 * s + grp;
+      f32x4 st[NB][2];
+      scores(t, st);
+      pv(t - 2);
+      softmax_full(st, false);
+    }
+    if (s_hot_end > 1) tprev = 2 * (s_hot_end - 1) + grp;
+    for (int s = s_hot_end > 1 ? s_hot_end : 1; s <= nsteps; ++s) generic_step(s);
+    // the last issued loads target unused slots; drain them before the ring is reused
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  block_barrier();
+
+  // ---- merge the two wave groups (same rows, alternate tiles) through LDS
+  float* xo = reinterpret_cast<float*>(ring);               // [wq][nb][db][lane][4]
+  float* xm = xo + 4 * NB * DB * 64 * 4;                    // [wq][nb][lane][2]
+  if (grp == 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(xo + (((wq * NB + nb) * DB + db) * 64 + lane) * 4) = o[nb][db];
+      xm[((wq * NB + nb) * 64 + lane) * 2 + 0] = mrun[nb];
+      xm[((wq * NB + nb) * 64 + lane) * 2 + 1] = lrun[nb];
+    }
+  }
+  block_barrier();
+  if (grp == 1) return;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float m1 = xm[((wq * NB + nb) * 64 + lane) * 2 + 0];
+    const float l1 = xm[((wq * NB + nb) * 64 + lane) * 2 + 1];
+    const float m0 = mrun[nb];
+    const float M = fmaxf(m0, m1);
+    const float a0 = (m0 == -INFINITY) ? 0.f : fast_exp2(m0 - M);
+    const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - M);
+    lrun[nb] = a0 * lrun[nb] + a1 * l1;
+    mrun[nb] = M;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + (((wq * NB + nb) * DB + db) * 64 + lane) * 4);
+      o[nb][db] = o[nb][db] * a0 + o1 * a1;
+    }
   }
 
   // ---- epilogue: lane holds O^T[d = 16 db + 4 q4 + i][row l16]
@@ -303,7 +486,7 @@ __global__ __launch_bounds__(kMfmaThreads) void k_attn_mfma(AttnArgs a) {
     float lsum = lrun[nb];
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-    const int m = rowbase + 16 * nb + l16;
+    const int m = row0 + row_l[nb];
     if (m >= a.R) continue;
     const int r = row_r[nb];
     if (a.n_split == 1) {
@@ -330,10 +513,10 @@ __global__ __launch_bounds__(kMfmaThreads) void k_attn_mfma(AttnArgs a) {
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
-  const int rows_per_wg = a.rows_per_wg;
-  const dim3 grid(a.n_split, a.row_chunks, a.B * a.Hkv);
-  const dim3 block(kMfmaThreads);
-  if (rows_per_wg == 128) {
+  const int64_t nwg = (int64_t)a.n_split * a.row_chunks * a.B * a.Hkv;
+  const dim3 grid((unsigned)nwg);
+  const dim3 block(512);
+  if (a.rows_per_wg == 128) {
     if (a.D == 128) hipLaunchKernelGGL((k_attn_mfma<128, 2>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_attn_mfma<64, 2>), grid, block, 0, st, a);
   } else {
