@@ -10,9 +10,20 @@ sets (~1.3 GB) are cycled so that the 256 MB last-level cache cannot hold a
 step's working set.  The metric is speculative query tokens verified per
 second (sum of valid block rows / step time).
 
+The K/V cache is laid out head-major, [B, Hkv, lmax, D] (each kv-head's keys
+contiguous), which the library takes through the descriptor's strides
+(--layout blhd selects token-major [B, lmax, Hkv, D]).
+
 Printed: one JSON line on stdout; details on stderr.  The roofline object
 describes the attention kernel (the dominant one): algorithmic bytes per
 launch / its mean duration, timed with HIP events on the launch stream.
+
+Counter runs: with --calibrate-copy the run also performs a 1 GiB
+device-to-device copy (a plain copy kernel of known size) before the timed
+steps, so that one `rocprofv3 --pmc FETCH_SIZE` run and one
+`rocprofv3 --pmc WRITE_SIZE` run see both kernels; `bench.py --summarize-pmc
+DIR` then scales the attention kernel's counters by the copy's known size and
+records the HBM bytes per launch in profiles/ with a hash of the kernel source.
 """
 
 from __future__ import annotations
@@ -73,6 +84,56 @@ def attention_flops(cfg, x) -> int:
     return total * 4 * cfg.D
 
 
+COPY_BYTES = 1 << 30
+
+
+def summarize_pmc(d: str):
+    """Per-launch HBM traffic of the attention kernel from rocprofv3 counter CSVs in d
+    (a FETCH_SIZE run and a WRITE_SIZE run of `bench.py --calibrate-copy`)."""
+    import csv
+    import glob
+
+    files = []
+    for one in d.split(","):
+        files += glob.glob(os.path.join(one, "**", "*counter_collection.csv"), recursive=True)
+    rows = [r for f in files for r in csv.DictReader(open(f))]
+    # the calibration copy is the copy dispatch with the largest grid (smaller ones are uploads)
+    copy_grid = max((int(r["Grid_Size"]) for r in rows if "copyBuffer" in r["Kernel_Name"]), default=-1)
+    vals = {}
+    for r in rows:
+        name, ctr = r["Kernel_Name"], r["Counter_Name"]
+        kind = None
+        if "k_attn_mfma" in name:
+            kind = "attn"
+        elif "copyBuffer" in name and int(r["Grid_Size"]) == copy_grid:
+            kind = "copy"
+        if kind and ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals.setdefault((kind, ctr), []).append(float(r["Counter_Value"]))
+    need = [("attn", "FETCH_SIZE"), ("attn", "WRITE_SIZE"), ("copy", "FETCH_SIZE"), ("copy", "WRITE_SIZE")]
+    missing = [k for k in need if k not in vals]
+    if missing:
+        raise SystemExit(f"counters missing in {d}: {missing}")
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    # the copy kernel moves COPY_BYTES each way: scale KiB readings to bytes of traffic
+    f_fetch = COPY_BYTES / (mean[("copy", "FETCH_SIZE")] * 1024)
+    f_write = COPY_BYTES / (mean[("copy", "WRITE_SIZE")] * 1024)
+    fetch = mean[("attn", "FETCH_SIZE")] * 1024 * f_fetch
+    write = mean[("attn", "WRITE_SIZE")] * 1024 * f_write
+    rec = {
+        "kernel": "k_attn_mfma", "workload": WORKLOAD,
+        "kernel_src_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+        "fetch_size_kib_per_launch": mean[("attn", "FETCH_SIZE")],
+        "write_size_kib_per_launch": mean[("attn", "WRITE_SIZE")],
+        "copy_fetch_size_kib": mean[("copy", "FETCH_SIZE")], "copy_write_size_kib": mean[("copy", "WRITE_SIZE")],
+        "copy_bytes": COPY_BYTES, "fetch_scale": f_fetch, "write_scale": f_write,
+        "traffic_bytes_per_launch": fetch + write,
+        "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+    }
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def counters_traffic():
     """HBM bytes per attention launch from committed rocprofv3 counter runs, or None
     if the kernel source changed since they were taken."""
@@ -118,10 +179,19 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=3, help="input sets cycled between steps")
-    ap.add_argument("--cpu-requests", type=int, default=6, help="requests in the oracle's timed sample")
+    ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0)
+    ap.add_argument("--layout", choices=("bhld", "blhd"), default="bhld")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-pmc", metavar="DIRS",
+                    help="comma-separated rocprofv3 output dirs of the FETCH_SIZE and WRITE_SIZE runs: "
+                         "write the traffic record and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -140,7 +210,7 @@ def main():
     t0 = time.time()
     for i in range(args.sets):
         x = wl.generate(cfg, seed=cfg.seed + 100 * i)
-        st = VerifyStep(cfg, x, device="cuda:0", kv_splits=args.kv_splits)
+        st = VerifyStep(cfg, x, device="cuda:0", kv_splits=args.kv_splits, layout=args.layout)
         steps_state.append((st, x))
     torch.cuda.synchronize()
     log(f"inputs: {args.sets} sets generated and uploaded in {time.time() - t0:.1f}s")
@@ -150,6 +220,12 @@ def main():
     flops = attention_flops(cfg, x0)
 
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         steps_state[i % args.sets][0].run(stream)
     torch.cuda.synchronize()
@@ -194,7 +270,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "ConFu-shaped Llama-3-8B verify: batch 16, 32q/8kv heads, head_dim 128, "
                                "prefix 4096 + 16 soft rows, 30-node tree + 30 contemplate rows, vocab 128256",
-                   "global_batch": cfg.B, "seq_len": 4096, "query_rows": cfg.Tq, "parallelism": "single GPU"},
+                   "global_batch": cfg.B, "seq_len": 4096, "query_rows": cfg.Tq, "kv_layout": args.layout,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counters_traffic(),
                      "kernel": "k_attn_mfma", "algorithmic_bytes_per_launch": alg_bytes,

@@ -45,7 +45,11 @@ class VerifyStep:
     """One verification step's device state for a workload."""
 
     def __init__(self, cfg: VerifyConfig, x: Dict[str, np.ndarray], device="cuda", kv_splits: int = 0,
-                 scale: float = 0.0, max_depth: Optional[int] = None):
+                 scale: float = 0.0, max_depth: Optional[int] = None, layout: str = "blhd"):
+        """``layout`` of the K/V cache in HBM: "blhd" = [B, lmax, Hkv, D] (token-major, the
+        generator's order) or "bhld" = [B, Hkv, lmax, D] (head-major).  Both are passed to
+        the library through the descriptor's strides; ``cache_host()`` returns the
+        cache in the generator's order either way."""
         self.cfg = cfg
         self.device = torch.device(device)
         dt = cfg.dtype
@@ -56,8 +60,14 @@ class VerifyStep:
         self.lmax = x["k_cache"].shape[1]
         self.max_depth = int(max_depth if max_depth is not None else min(cfg.max_depth, bd.SPEC_MAX_DEPTH))
         self.q = to_device(x["q"], dt, dev)
+        if layout not in ("blhd", "bhld"):
+            raise ValueError(layout)
+        self.layout = layout
         self.k_cache = to_device(x["k_cache"], dt, dev)
         self.v_cache = to_device(x["v_cache"], dt, dev)
+        if layout == "bhld":
+            self.k_cache = self.k_cache.permute(0, 2, 1, 3).contiguous()
+            self.v_cache = self.v_cache.permute(0, 2, 1, 3).contiguous()
         self.k_blk = to_device(x["k_blk"], dt, dev)
         self.v_blk = to_device(x["v_blk"], dt, dev)
         self.k_soft = to_device(x["k_soft"], dt, dev) if cfg.S else None
@@ -83,11 +93,20 @@ class VerifyStep:
         self.cache_len_out = torch.empty(self.B, **i32)
 
         Hkv, D = cfg.Hkv, cfg.D
+        strides = ((self.lmax * Hkv * D, Hkv * D, D) if layout == "blhd"
+                   else (Hkv * self.lmax * D, D, self.lmax * D))
         self.desc = bd.make_desc(self.B, self.Tq, cfg.Hq, Hkv, D, cfg.S, DTYPE_CODE[dt], self.lmax,
-                                 (self.lmax * Hkv * D, Hkv * D, D), scale=scale, kv_splits=kv_splits)
+                                 strides, scale=scale, kv_splits=kv_splits)
         self.ws_bytes = bd.spec_verify_attn_workspace(self.desc)
         self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
                           if self.ws_bytes else None)
+
+    def cache_host(self):
+        """(k_cache, v_cache) as host arrays in the generator's [B, lmax, Hkv, D] order."""
+        k, v = self.k_cache, self.v_cache
+        if self.layout == "bhld":
+            k, v = k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)
+        return to_host_bits(k.contiguous()), to_host_bits(v.contiguous())
 
     # -- the four entry points
     def build_mask(self, stream=None):

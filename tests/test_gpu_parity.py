@@ -259,3 +259,69 @@ def test_full_step_chain_matches_oracle():
                                            x["acc_parent"], st.max_depth)
     np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
     np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
+
+
+@pytest.mark.parametrize("name", ["c1_tiny_la", "c2_la_7b", "c3_confu_8b", "c4_tree_3b", "c5_stream_70b"])
+def test_head_major_cache_layout(name):
+    # the cache may be [B, Hkv, lmax, D] (head-major) through the descriptor's strides
+    cfg = wl.CONFIGS[name]
+    x = wl.generate(cfg, B=min(cfg.B, 2), L=(70, 140) if cfg.L[0] else None)
+    st = VerifyStep(cfg, x, layout="bhld")
+    st.run()
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_attention(x, cfg)
+    compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
+    greedy, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                           x["acc_parent"], st.max_depth)
+    kc, vc, L2 = oracle.commit_kv(x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"], A, path)
+    np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L2)
+    k_host, v_host = st.cache_host()
+    np.testing.assert_array_equal(k_host, kc)
+    np.testing.assert_array_equal(v_host, vc)
+
+
+FULL_SAMPLES = {
+    # name: (requests, rows) sampled for the oracle; rows include first/last and contemplate rows
+    "c2_la_7b": ([0, 3, 7], [0, 3, 7]),
+    "c3_confu_8b": ([0, 7, 15], [0, 1, 17, 29, 30, 45, 59]),
+    "c4_tree_3b": ([0, 19, 31], [0, 31, 59, 60, 90, 119]),
+    "c5_stream_70b": ([0, 15], [0, 3, 64, 127]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FULL_SAMPLES))
+def test_full_size_sampled(name):
+    """Whole workload at its full size in the benchmark's launch configuration
+    (automatic split, head-major cache); attention checked on sampled rows, the
+    argmax / acceptance / commit checked everywhere."""
+    cfg = wl.CONFIGS[name]
+    reqs, rows = FULL_SAMPLES[name]
+    say(f"[gpu] full-size {name}: generate")
+    x = wl.generate(cfg)
+    st = VerifyStep(cfg, x, layout="bhld")
+    say(f"[gpu] full-size {name}: run step (ws {st.ws_bytes} B)")
+    st.run()
+    torch.cuda.synchronize()
+    bits, sp = oracle.build_mask(x["attn_parent"], x["sp_flag"], x["n_q"])
+    np.testing.assert_array_equal(st.mask_bits.cpu().numpy().view(np.uint32), bits)
+    np.testing.assert_array_equal(st.sp_bits.cpu().numpy().view(np.uint32), sp)
+    say(f"[gpu] full-size {name}: oracle on sampled rows")
+    ref, ref_lse = oracle_attention(x, cfg, requests=reqs, rows=rows)
+    compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x, rows=rows, requests=reqs)
+    out = st.out.cpu().numpy()
+    assert np.isfinite(out).all()
+    say(f"[gpu] full-size {name}: acceptance and commit")
+    greedy, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                           x["acc_parent"], st.max_depth)
+    np.testing.assert_array_equal(st.argmax.cpu().numpy(), greedy)
+    np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
+    np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
+    L = x["cache_len"]
+    np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L + A)
+    k_host, v_host = st.cache_host()
+    for b in range(cfg.B):
+        for d in range(int(A[b])):
+            np.testing.assert_array_equal(k_host[b, L[b] + d], x["k_blk"][b, path[b, d]])
+            np.testing.assert_array_equal(v_host[b, L[b] + d], x["v_blk"][b, path[b, d]])
+        np.testing.assert_array_equal(k_host[b, :L[b]], x["k_cache"][b, :L[b]])
+    say(f"    accepted lengths {A.tolist()}")
