@@ -3,10 +3,11 @@
 // k_argmax: the greedy target token of every node -- the index of its row's
 // largest logit ("Speculative Streaming", the verification step: hard
 // matching against the target's most likely token; "Lookahead Attention"
-// 2.3).  One workgroup per node row streams the vocabulary with 16-byte loads;
-// each thread keeps its best (value, index) in increasing index order, and
-// the workgroup reduces with the rule "larger value, then lower index", so
-// ties resolve to the lowest index and -0 compares equal to +0.
+// 2.3).  One workgroup per node row streams the vocabulary with 16-byte loads,
+// eight in flight per thread; each thread keeps its best (value, index) in
+// increasing index order, and the workgroup reduces with the rule "larger
+// value, then lower index", so ties resolve to the lowest index and -0
+// compares equal to +0.
 //
 // k_accept: one workgroup per request, one thread per node.  Each thread
 // walks its node's path to the root: the node is accepted iff every node on
@@ -41,11 +42,35 @@ __device__ __forceinline__ float elem_at<uint16_t>(const uint16_t* p, int i) {
   return __uint_as_float(uint32_t(p[i]) << 16);
 }
 
+// Within one thread the indices it visits only increase, so a strict ">" keeps
+// the first maximum; the full rule is needed only when merging threads.
+__device__ __forceinline__ void first_max(float& bv, int& bi, float v, int i) {
+  const bool gt = v > bv;
+  bv = gt ? v : bv;
+  bi = gt ? i : bi;
+}
+
+template <typename T>
+__device__ __forceinline__ void scan16(float& bv, int& bi, const u32x4& x, int i0) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      first_max(bv, bi, bf16lo(w[e]), i0 + 2 * e);
+      first_max(bv, bi, bf16hi(w[e]), i0 + 2 * e + 1);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) first_max(bv, bi, __uint_as_float(w[e]), i0 + e);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ logits, int T_, int V,
                                                         const int32_t* __restrict__ n_nodes,
                                                         int32_t* __restrict__ out) {
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
+  constexpr int U = 8;               // 16-byte loads in flight per thread
   __shared__ float sv_[kArgThreads / kWave];
   __shared__ int si_[kArgThreads / kWave];
   const int row = blockIdx.x;
@@ -59,49 +84,28 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ lo
   const T* base = logits + (int64_t)row * V;
   const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
   const int pre = min(V, mis == 0 ? 0 : E - mis);
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < pre; i += kArgThreads) better(bv, bi, elem_at<T>(base, i), i);
+  // two independent running maxima (even / odd load slots) shorten the dependency chain
+  float bv0 = -INFINITY, bv1 = -INFINITY;
+  int bi0 = 0x7fffffff, bi1 = 0x7fffffff;
+  for (int i = threadIdx.x; i < pre; i += kArgThreads) first_max(bv0, bi0, elem_at<T>(base, i), i);
   const int nvec = (V - pre) / E;
   const char* vb = reinterpret_cast<const char*>(base + pre);
-  constexpr int U = 4;
   int k = threadIdx.x;
   for (; k + (U - 1) * kArgThreads < nvec; k += U * kArgThreads) {
     u32x4 x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) x[u] = ldg16(vb + (int64_t)(k + u * kArgThreads) * 16);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i0 = pre + (k + u * kArgThreads) * E;
-      const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          better(bv, bi, bf16lo(w[e]), i0 + 2 * e);
-          better(bv, bi, bf16hi(w[e]), i0 + 2 * e + 1);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) better(bv, bi, __uint_as_float(w[e]), i0 + e);
-      }
+    for (int u = 0; u < U; u += 2) {
+      scan16<T>(bv0, bi0, x[u], pre + (k + u * kArgThreads) * E);
+      scan16<T>(bv1, bi1, x[u + 1], pre + (k + (u + 1) * kArgThreads) * E);
     }
   }
-  for (; k < nvec; k += kArgThreads) {
-    const u32x4 x = ldg16(vb + (int64_t)k * 16);
-    const int i0 = pre + k * E;
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        better(bv, bi, bf16lo(w[e]), i0 + 2 * e);
-        better(bv, bi, bf16hi(w[e]), i0 + 2 * e + 1);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) better(bv, bi, __uint_as_float(w[e]), i0 + e);
-    }
-  }
-  for (int i = pre + nvec * E + threadIdx.x; i < V; i += kArgThreads) better(bv, bi, elem_at<T>(base, i), i);
+  for (; k < nvec; k += kArgThreads) scan16<T>(bv0, bi0, ldg16(vb + (int64_t)k * 16), pre + k * E);
+  for (int i = pre + nvec * E + threadIdx.x; i < V; i += kArgThreads) first_max(bv1, bi1, elem_at<T>(base, i), i);
+  float bv = bv0;
+  int bi = bi0;
+  better(bv, bi, bv1, bi1);
 
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -117,7 +121,8 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ lo
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kArgThreads / kWave; ++w) better(bv, bi, sv_[w], si_[w]);
-    out[row] = bi;
+    // a row of -inf only: every element ties, the first index wins
+    out[row] = bi == 0x7fffffff ? 0 : bi;
   }
 }
 
