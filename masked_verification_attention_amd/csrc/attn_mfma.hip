@@ -16,20 +16,28 @@
 //   word.  A workgroup owns 64 * NB rows and has 8 waves in two groups of 4;
 //   wave w of a group owns NB blocks of 16 rows.  The two groups take
 //   alternate 32-key tiles of the same key stream (a split of the keys inside
-//   the workgroup) and merge their softmax states through LDS at the end, so
-//   every SIMD runs two waves whose matrix and vector phases interleave.
+//   the workgroup) and merge their softmax states through LDS at the end.
+//
+// Schedule (ping-pong of the two groups)
+//   A step of a group is a matrix half -- scores of its tile, P*V of its
+//   previous tile -- then a barrier, then a softmax half.  Group 1 passes one
+//   extra barrier before its first step, so it runs half a step behind group
+//   0: while one group's waves feed the matrix cores the other group's waves
+//   (on the same SIMDs) run their exponentials, and the two kinds of work
+//   overlap without the compiler having to interleave them.
 //
 // Key stream
 //   Keys are the prefix range of this split, then -- last split only -- the S
 //   soft keys and the block rows.  Segments are tiled separately, so prefix
-//   tiles need no mask except the ragged tail.  Tiles are copied straight from
-//   HBM into a ring of LDS slots with 16-byte direct-to-LDS loads, four tiles
-//   ahead of the compute, one barrier per pair of tiles.  Each wave is
-//   software-pipelined: the scores of its tile t are computed while the P*V
-//   product of its tile t-1 runs, so matrix and vector work overlap.  K and V sit
-//   row-major in a slot with the 16-byte chunks of key row k stored at chunk
-//   position (c ^ k mod 16), which keeps both read patterns below free of bank
-//   conflicts:
+//   tiles need no mask except the ragged tail.  Each group copies its own
+//   tiles straight from HBM into rings of LDS slots (one for K, one for V) with
+//   16-byte direct-to-LDS loads, three steps ahead of the compute; a wave
+//   issues its share of a step's loads half in its matrix half and half spread
+//   through its softmax half, since a burst of such loads stalls the issuing
+//   wave for hundreds of cycles.  K and V sit
+//   row-major in a slot with 16-byte chunk c of key row k stored at chunk
+//   position c ^ swz(k), an XOR map chosen so that both read patterns below are
+//   free of bank conflicts:
 //     S^T = K Q^T : K is the A operand, one 16-byte read per lane;
 //     O^T = V^T P^T : V^T is the A operand, built by the transposing 64-bit
 //                     LDS read (lane j of a 16-lane group receives element
@@ -61,16 +69,28 @@ struct MfmaCfg {
   static constexpr int CH = D / 8;               // 16-byte chunks per key row
   static constexpr int ROWB = D * 2;             // bytes per key row
   static constexpr int TILEB = TK * ROWB;        // bytes of a K (or V) tile
-  static constexpr int STAGEB = 2 * TILEB;       // K + V
   static constexpr int RPI = 64 / CH;            // key rows per 1 KB wave load
-  static constexpr int IPT = 2 * TK / RPI;       // wave loads per tile (K and V)
-  static constexpr int LPW = IPT / kWaves;       // wave loads per wave per tile
-  static constexpr int P = 4;                    // tiles in flight
-  static constexpr int NS = P + 4;               // ring slots: 2 scored + 2 awaiting P*V + P in flight
-  static constexpr bool kIssueLate = false;      // issue a step's loads after its compute
+  static constexpr int LPT = TK / RPI;           // wave loads per K (or V) tile
+  static constexpr int LPS = 2 * LPT / 4;        // wave loads per wave per step (a group's K + V tile over its 4 waves)
+  static constexpr int P = 6;                    // tiles in flight per ring (P / 2 steps ahead)
+  static constexpr int NSK = P + 2;              // K slots: P in flight + the 2 being scored
+  static constexpr int NSV = P + 2;              // V slots: P in flight + the 2 in P*V
   static constexpr int ROWS = 64 * NB;           // rows per workgroup
   static constexpr int MAXW = (SPEC_MAX_TQ + 31) / 32;
-  static_assert(LPW >= 1 && IPT % kWaves == 0, "tile loads must split evenly over the waves");
+  static_assert(LPS >= 1 && (2 * LPT) % 4 == 0 && LPT % LPS == 0,
+                "each wave's loads of a step must fall in one tile");
+  // chunk position of 16-byte chunk c of key row r is c ^ swz(r).  For 256-byte
+  // rows this is the GF(2)-linear map with columns 3, 10, 4, 12 on the row's low
+  // four bits: measured free of bank conflicts both for the 16-byte K reads (16
+  // consecutive rows, one chunk) and for the transposing V reads (4 rows of two
+  // adjacent chunks per 16 lanes), where plain c ^ (r mod 16) costs the V read
+  // 2-way conflicts.  128-byte rows keep c ^ (r mod 8).
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (CH == 16)
+      return ((r & 1) ? 3 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 4 : 0) ^ ((r & 8) ? 12 : 0);
+    else
+      return r & (CH - 1);
+  }
 };
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -119,7 +139,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   using C = MfmaCfg<D, NB>;
   constexpr int DC = D / 32;   // k-chunks of S^T = K Q^T
   constexpr int DB = D / 16;   // 16-wide head-dim blocks of O^T
-  __shared__ __attribute__((aligned(1024))) char ring[C::NS * C::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char ring[(C::NSK + C::NSV) * C::TILEB];
   __shared__ uint32_t mask_lds[C::ROWS][C::MAXW];
 
   // ---- which (split, request, kv-head, row chunk): siblings of a row chunk
@@ -183,59 +203,77 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     }
   }
 
-  // ---- direct-to-LDS tile loads
+  // ---- direct-to-LDS tile loads.  Group g's "step u loads" are what it reads
+  // at step u: K of its tile 2u+g (scored at step u) and V of its tile 2u+g-2
+  // (whose P*V runs at step u).  Waves 0..3 and 4..7 of the group split the K
+  // and V streams, LPS 1 KB wave loads each.
   const char* kc = static_cast<const char*>(a.k_cache) + ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
   const char* vc = static_cast<const char*>(a.v_cache) + ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
   const char* kblk = static_cast<const char*>(a.k_blk) + ((int64_t)b * a.Tq * a.Hkv + h) * D * 2;
   const char* vblk = static_cast<const char*>(a.v_blk) + ((int64_t)b * a.Tq * a.Hkv + h) * D * 2;
   const char* ksoft = static_cast<const char*>(a.k_soft) + (int64_t)h * D * 2;
   const char* vsoft = static_cast<const char*>(a.v_soft) + (int64_t)h * D * 2;
-  const int lrow = lane / C::CH;          // key row within the wave's 1 KB load
-  const int lpos = lane % C::CH;          // chunk position the lane fills
-  // per-tile source of its key rows (uniform); rows past the segment end are
-  // clamped to its last key and masked out in the compute
+  const int gw = wave & 3;                        // wave within its group
+  const bool load_v = (gw * C::LPS) / C::LPT >= 1;   // first half of the group loads K, second V
+  const int lrow = lane / C::CH;               // key row within the wave's 1 KB load
+  const int lpos = lane % C::CH;               // chunk position the lane fills
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_char*)ring;
-  int lane_row[C::LPW], lane_off[C::LPW];   // per load: key row in the tile, byte offset of its chunk
+  const char* const kring = ring;
+  const char* const vring = ring + C::NSK * C::TILEB;
+  int lane_row[C::LPS], lane_off[C::LPS], lane_dst[C::LPS];
 #pragma unroll
-  for (int j = 0; j < C::LPW; ++j) {
-    const int ii = (wave * C::LPW + j) % (C::IPT / 2);
+  for (int j = 0; j < C::LPS; ++j) {
+    const int ii = (gw * C::LPS + j) % C::LPT;
     lane_row[j] = ii * C::RPI + lrow;
-    lane_off[j] = (lpos ^ (lane_row[j] & (C::CH - 1))) * 16;
+    lane_off[j] = (lpos ^ C::swz(lane_row[j])) * 16;
+    lane_dst[j] = ii * 1024;
   }
-  auto issue_tile = [&](int t) {
-    const int ti = t < nt ? t : nt - 1;   // past the end: reload the last tile into an unused slot
-    const char* bk;
-    const char* bv;
+  // Rows past a segment's end are clamped to its last key and masked in the
+  // compute.  A tile past the end still issues its loads (the last tile again,
+  // into the slot that tile index maps to, which nothing reads): the waits
+  // below count loads, and a wait for "all but the newest step's loads" only
+  // covers an older step if the newer one really issued its share.  Tiles
+  // before the start (V in the first two steps) issue nothing; a non-empty
+  // step always follows them.
+  struct TileSrc {
+    const char* base;
     int stride, nvalid;
-    if (ti < ntp) {
-      const int key0 = ks + ti * C::TK;
-      bk = kc + (int64_t)key0 * a.sl * 2;
-      bv = vc + (int64_t)key0 * a.sl * 2;
-      stride = (int)(a.sl * 2);
-      nvalid = ke - key0;
-    } else if (ti < ntp + nts) {
-      const int key0 = (ti - ntp) * C::TK;
-      bk = ksoft + (int64_t)key0 * a.Hkv * D * 2;
-      bv = vsoft + (int64_t)key0 * a.Hkv * D * 2;
-      stride = a.Hkv * D * 2;
-      nvalid = a.S - key0;
+    uint32_t slot;
+    bool on;
+  };
+  auto tile_src = [&](int u) __attribute__((always_inline)) {
+    TileSrc r;
+    const int tslot = 2 * u + grp - (load_v ? 2 : 0);
+    r.on = tslot >= 0;
+    const int t = min(max(tslot, 0), nt - 1);
+    if (t < ntp) {
+      const int key0 = ks + t * C::TK;
+      r.base = (load_v ? vc : kc) + (int64_t)key0 * a.sl * 2;
+      r.stride = (int)(a.sl * 2);
+      r.nvalid = ke - key0;
+    } else if (t < ntp + nts) {
+      const int key0 = (t - ntp) * C::TK;
+      r.base = (load_v ? vsoft : ksoft) + (int64_t)key0 * a.Hkv * D * 2;
+      r.stride = a.Hkv * D * 2;
+      r.nvalid = a.S - key0;
     } else {
-      const int key0 = (ti - ntp - nts) * C::TK;
-      bk = kblk + (int64_t)key0 * a.Hkv * D * 2;
-      bv = vblk + (int64_t)key0 * a.Hkv * D * 2;
-      stride = a.Hkv * D * 2;
-      nvalid = nq - key0;
+      const int key0 = (t - ntp - nts) * C::TK;
+      r.base = (load_v ? vblk : kblk) + (int64_t)key0 * a.Hkv * D * 2;
+      r.stride = a.Hkv * D * 2;
+      r.nvalid = nq - key0;
     }
-    const uint32_t slot = ring_lds + (t % C::NS) * C::STAGEB;
+    r.slot = ring_lds + (load_v ? (C::NSK + max(tslot, 0) % C::NSV) : (max(tslot, 0) % C::NSK)) * C::TILEB;
+    return r;
+  };
+  auto issue_one = [&](const TileSrc& r, int j) __attribute__((always_inline)) {
+    if (!r.on) return;
+    const int rel = min(lane_row[j], r.nvalid - 1);
+    dma16(r.slot + lane_dst[j], r.base + (rel * r.stride + lane_off[j]));
+  };
+  auto issue_step = [&](int u) __attribute__((always_inline)) {
+    const TileSrc r = tile_src(u);
 #pragma unroll
-    for (int j = 0; j < C::LPW; ++j) {
-      const int ins = wave * C::LPW + j;             // 0 .. IPT-1
-      const bool is_v = ins >= C::IPT / 2;
-      const int ii = is_v ? ins - C::IPT / 2 : ins;
-      const int rel = min(lane_row[j], nvalid - 1);
-      const char* src = (is_v ? bv : bk) + (rel * stride + lane_off[j]);
-      dma16(slot + (is_v ? C::TILEB : 0) + ii * 1024, src);
-    }
+    for (int j = 0; j < C::LPS; ++j) issue_one(r, j);
   };
 
   float mrun[NB], lrun[NB], negm[NB];
@@ -256,35 +294,42 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 
   const float P_LIMIT = 256.0f;   // 2^TAU with TAU = 8: bound on any probability between rescales
   if (nt > 0) {
-#pragma unroll
-    for (int t = 0; t < C::P; ++t) issue_tile(t);
+    // Ping-pong of the two wave groups (group g owns tiles 2s+g).  Between any
+    // two barriers one group runs its matrix half (scores of one tile, P*V of
+    // its previous tile) while the other runs its softmax half, so each SIMD
+    // holds one wave on the matrix cores and one on the vector ALUs.
     const int nsteps = (nt + 1) / 2;
+    f32x4 st[NB][2];
     bf16x8 pf[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) pf[nb] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-    int tprev = -1;   // this wave's tile whose P*V is still to be done
+    for (int nb = 0; nb < NB; ++nb) {
+      pf[nb] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) st[nb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < C::P / 2; ++u) issue_step(u);
 
-    // step s: wait for tiles 2s, 2s+1, free the slots read two steps ago, refill
-    auto begin_step = [&](int s) {
-      wait_vmcnt<(C::P - 2) * C::LPW>();
+    // step s: wait for step s's loads, free the slots read at step s-1, refill
+    auto begin_step = [&](int s) __attribute__((always_inline)) {
+      wait_vmcnt<(C::P / 2 - 1) * C::LPS>();
       block_barrier();
-      issue_tile(2 * s + C::P);
-      issue_tile(2 * s + C::P + 1);
     };
-    // S^T = K Q^T for tile t
-    auto scores = [&](int t, f32x4 (&st)[NB][2]) {
-      const char* slotK = ring + (t % C::NS) * C::STAGEB;
-      // K fragments: key 16 kb + l16, head dims 32 dc + 8 q4 .. +7
-      bf16x8 kf[2][DC];
+    // K fragments of tile t: key 16 kb + l16, head dims 32 dc + 8 q4 .. +7
+    auto read_k = [&](int t, bf16x8 (&kf)[2][DC]) __attribute__((always_inline)) {
+      const char* slotK = kring + (t % C::NSK) * C::TILEB;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int row = 16 * kb + l16;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          const int ch = (4 * dc + q4) ^ (row & (C::CH - 1));
+          const int ch = (4 * dc + q4) ^ C::swz(row);
           kf[kb][dc] = as_bf16x8(*reinterpret_cast<const u32x4*>(slotK + row * C::ROWB + ch * 16));
         }
       }
+    };
+    // S^T = K Q^T
+    auto scores = [&](const bf16x8 (&kf)[2][DC], f32x4 (&sc)[NB][2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -292,33 +337,38 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int dc = 0; dc < DC; ++dc) acc = mfma16x16x32(kf[kb][dc], qf[nb][dc], acc);
-          st[nb][kb] = acc;
+          sc[nb][kb] = acc;
         }
     };
-    // O^T += V^T P^T for tile tp; V^T fragment for head dims 16 db + l16 and
-    // keys {4 q4 .. +3} (read 0) and {16 + 4 q4 .. +3} (read 1)
-    auto pv = [&](int tp) {
-      const char* slotV = ring + (tp % C::NS) * C::STAGEB + C::TILEB;
+    // V^T fragments of tile tp: head dims 16 db + l16 and keys {4 q4 .. +3}
+    // (read 0) and {16 + 4 q4 .. +3} (read 1)
+    auto read_v = [&](int tp, bf16x8 (&vf)[DB]) __attribute__((always_inline)) {
+      const char* slotV = vring + (tp % C::NSV) * C::TILEB;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         uint32_t vw[4];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           const int row = 16 * cc + 4 * q4 + (l16 >> 2);
-          const int ch = (2 * db + ((l16 & 3) >> 1)) ^ (row & (C::CH - 1));
-          lds_char* p = to_lds(slotV) + row * C::ROWB + ch * 16 + 8 * (l16 & 1);
-          const bf16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+          const int ch = (2 * db + ((l16 & 3) >> 1)) ^ C::swz(row);
+          lds_char* ptr = to_lds(slotV) + row * C::ROWB + ch * 16 + 8 * (l16 & 1);
+          const bf16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)ptr);
           uint32_t w2[2];
           __builtin_memcpy(w2, &v4, 8);
           vw[2 * cc] = w2[0];
           vw[2 * cc + 1] = w2[1];
         }
-        const bf16x8 vf = as_bf16x8(u32x4{vw[0], vw[1], vw[2], vw[3]});
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb][db] = mfma16x16x32(vf, pf[nb], o[nb][db]);
+        vf[db] = as_bf16x8(u32x4{vw[0], vw[1], vw[2], vw[3]});
       }
     };
-    auto pack = [&](int nb, const float (&p)[8]) {
+    // O^T += V^T P^T
+    auto pv = [&](const bf16x8 (&vf)[DB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nb][db] = mfma16x16x32(vf[db], pf[nb], o[nb][db]);
+    };
+    auto pack = [&](int nb, const float (&p)[8]) __attribute__((always_inline)) {
       typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
       uint32_t pk[4];
 #pragma unroll
@@ -331,7 +381,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       pf[nb] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
     };
     // exact max of row block nb over xs, rescale its state, and recompute p
-    auto rescale = [&](int nb, const float (&xs)[8], float (&p)[8], float& ps) {
+    auto rescale = [&](int nb, const float (&xs)[8], float (&p)[8], float& ps) __attribute__((always_inline)) {
       const float lmax = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])),
                                fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
       float mx = lmax * a.c;
@@ -352,15 +402,28 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     };
     // softmax of a complete prefix tile: no mask; probabilities against the current
     // max, whose sum exceeds 2^TAU whenever one of them could (then rescale exactly)
-    auto softmax_full = [&](const f32x4 (&st)[NB][2], bool first) {
+    // (src: when set, the step's loads are issued spread through the exponentials,
+    // so that no wave stalls on a burst of loads queued behind its neighbours')
+    auto softmax_full = [&](bool first, const TileSrc* src = nullptr) __attribute__((always_inline)) {
       float xs[NB][8], p[NB][8], ps[NB];
       bool need = first;
+      constexpr int kPieces = 2 * NB;   // halves of the row blocks' exponentials
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          xs[nb][e] = st[nb][e >> 2][e & 3];
-          p[nb][e] = fast_exp2(fmaf(xs[nb][e], a.c, negm[nb]));
+        for (int hh = 0; hh < 2; ++hh) {
+          if (src != nullptr) {
+            const int piece = 2 * nb + hh;
+#pragma unroll
+            for (int j = C::LPS / 2; j < C::LPS; ++j)
+              if ((j - C::LPS / 2) * kPieces / (C::LPS - C::LPS / 2) == piece) issue_one(*src, j);
+          }
+#pragma unroll
+          for (int e = 4 * hh; e < 4 * hh + 4; ++e) {
+            xs[nb][e] = st[nb][e >> 2][e & 3];
+            p[nb][e] = fast_exp2(fmaf(xs[nb][e], a.c, negm[nb]));
+          }
+          if (src != nullptr) __builtin_amdgcn_sched_barrier(0);
         }
         ps[nb] = ((p[nb][0] + p[nb][1]) + (p[nb][2] + p[nb][3])) + ((p[nb][4] + p[nb][5]) + (p[nb][6] + p[nb][7]));
         need = need || !(ps[nb] <= P_LIMIT);
@@ -376,7 +439,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       }
     };
     // softmax of a tile that needs masking: ragged prefix tail, soft prompt, block rows
-    auto softmax_masked = [&](int t, const f32x4 (&st)[NB][2], int seg, int lim) {
+    auto softmax_masked = [&](int t, int seg, int lim) __attribute__((always_inline)) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // visibility of the lane's 8 keys (tile keys 16 kb + 4 q4 + i) for its row
@@ -389,11 +452,9 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
           const uint32_t mw = mask_lds[row_l[nb]][t - ntp - nts];
           vis = ((mw >> (4 * q4)) & 0xfu) | (((mw >> (16 + 4 * q4)) & 0xfu) << 4);
         }
-        uint32_t lm = 0u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (((e < 4) ? 4 * q4 + e : 16 + 4 * q4 + e - 4) < lim) lm |= 1u << e;
-        vis &= lm;
+        // keys below lim: slots e < 4 hold keys 4 q4 + e, slots e >= 4 keys 16 + 4 q4 + e - 4
+        const int nlo = clampi(lim - 4 * q4, 0, 4), nhi = clampi(lim - 16 - 4 * q4, 0, 4);
+        vis &= ((1u << nlo) - 1u) | (((1u << nhi) - 1u) << 4);
         float xs[8], p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -406,49 +467,73 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         pack(nb, p);
       }
     };
-    // any step: the wave's tile may be missing, partial, soft or block
-    auto generic_step = [&](int s) {
-      begin_step(s);
+    auto softmax_any = [&](int t) __attribute__((always_inline)) {
+      const int seg = t < ntp ? 0 : (t < ntp + nts ? 1 : 2);
+      int lim;
+      if (seg == 0) lim = min(C::TK, ke - (ks + t * C::TK));
+      else if (seg == 1) lim = min(C::TK, a.S - (t - ntp) * C::TK);
+      else lim = min(C::TK, nq - (t - ntp - nts) * C::TK);
+      if (seg == 0 && lim == C::TK)
+        softmax_full(mrun[0] == -INFINITY || (NB > 1 && mrun[NB - 1] == -INFINITY));
+      else
+        softmax_masked(t, seg, lim);
+    };
+    // Step s of a group: its matrix half (scores of its tile 2s+g, P*V of its
+    // tile 2s+g-2), a barrier, its softmax half (of tile 2s+g).  Every wave runs
+    // the same sequence; group 1 passes one extra barrier first, so it runs half
+    // a step behind group 0 and the two groups' halves interleave.
+    auto matrix_half = [&](int s) __attribute__((always_inline)) {
       const int t = 2 * s + grp;
-      const bool cur = (s < nsteps) && (t < nt);
-      f32x4 st[NB][2];
-      if (cur) scores(t, st);
-      if (tprev >= 0) pv(tprev);
-      if (cur) {
-        const int seg = t < ntp ? 0 : (t < ntp + nts ? 1 : 2);
-        int lim;
-        if (seg == 0) lim = min(C::TK, ke - (ks + t * C::TK));
-        else if (seg == 1) lim = min(C::TK, a.S - (t - ntp) * C::TK);
-        else lim = min(C::TK, nq - (t - ntp - nts) * C::TK);
-        if (seg == 0 && lim == C::TK) softmax_full(st, mrun[0] == -INFINITY || (NB > 1 && mrun[NB - 1] == -INFINITY));
-        else softmax_masked(t, st, seg, lim);
-        tprev = t;
-      } else {
-        tprev = -1;
+      if (t < nt) {
+        bf16x8 kf[2][DC];
+        read_k(t, kf);
+        scores(kf, st);
+      }
+      if (s >= 1 && t - 2 < nt) {
+        bf16x8 vf[DB];
+        read_v(t - 2, vf);
+        pv(vf);
       }
     };
-
-    // steps whose two tiles are complete prefix tiles, after the first, run the
-    // branch-free form: scores, the previous tile's P*V, softmax
-    const int nfull = (ke - ks) / C::TK;
-    const int s_hot_end = nfull / 2;
-    generic_step(0);
-    for (int s = 1; s < s_hot_end; ++s) {
+    auto generic_step = [&](int s) __attribute__((always_inline)) {
       begin_step(s);
-      const int t = 2 * s + grp;
-      f32x4 st[NB][2];
-      scores(t, st);
-      pv(t - 2);
-      softmax_full(st, false);
-    }
-    if (s_hot_end > 1) tprev = 2 * (s_hot_end - 1) + grp;
-    for (int s = s_hot_end > 1 ? s_hot_end : 1; s <= nsteps; ++s) generic_step(s);
-    // the last issued loads target unused slots; drain them before the ring is reused
+      matrix_half(s);
+      block_barrier();
+      issue_step(s + C::P / 2);
+      if (2 * s + grp < nt) softmax_any(2 * s + grp);
+    };
+    // own tiles 2s+g (scored and softmaxed) and 2s+g-2 (in P*V) are full prefix
+    // tiles and 2s+g is not the group's first: no masks, no branches
+    auto hot_step = [&](int s) __attribute__((always_inline)) {
+      begin_step(s);
+      const TileSrc src = tile_src(s + C::P / 2);
+      // every fragment read goes out before the first matrix instruction, so
+      // the LDS latency is paid once per half; half of the step's loads follow
+      bf16x8 kf[2][DC], vf[DB];
+      read_k(2 * s + grp, kf);
+      read_v(2 * s + grp - 2, vf);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < C::LPS / 2; ++j) issue_one(src, j);
+      scores(kf, st);
+      pv(vf);
+      block_barrier();
+      softmax_full(false, &src);
+    };
+    const int nfull = (ke - ks) / C::TK;
+    const int s_hot_end = (nfull - grp + 1) / 2;   // steps whose own tile is a full prefix tile
+    if (grp == 1) block_barrier();
+    generic_step(0);
+    for (int s = 1; s < s_hot_end; ++s) hot_step(s);
+    for (int s = max(1, s_hot_end); s <= nsteps; ++s) generic_step(s);
+    if (grp == 0) block_barrier();
     __builtin_amdgcn_s_waitcnt(0);
   }
   block_barrier();
 
   // ---- merge the two wave groups (same rows, alternate tiles) through LDS
+  static_assert((4 * NB * DB * 64 * 4 + 4 * NB * 64 * 2) * 4 <= (C::NSK + C::NSV) * C::TILEB,
+                "merge scratch must fit in the ring");
   float* xo = reinterpret_cast<float*>(ring);               // [wq][nb][db][lane][4]
   float* xm = xo + 4 * NB * DB * 64 * 4;                    // [wq][nb][lane][2]
   if (grp == 1) {
