@@ -4,7 +4,7 @@
 // largest logit ("Speculative Streaming", the verification step: hard
 // matching against the target's most likely token; "Lookahead Attention"
 // 2.3).  One workgroup per node row streams the vocabulary with 16-byte loads,
-// eight in flight per thread; each thread keeps its best (value, index) in
+// two rounds of eight in flight per thread; each thread keeps its best (value, index) in
 // increasing index order, and the workgroup reduces with the rule "larger
 // value, then lower index", so ties resolve to the lowest index and -0
 // compares equal to +0.
@@ -90,18 +90,36 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ lo
   for (int i = threadIdx.x; i < pre; i += kArgThreads) first_max(bv0, bi0, elem_at<T>(base, i), i);
   const int nvec = (V - pre) / E;
   const char* vb = reinterpret_cast<const char*>(base + pre);
-  int k = threadIdx.x;
-  for (; k + (U - 1) * kArgThreads < nvec; k += U * kArgThreads) {
-    u32x4 x[U];
+  // Rounds of U loads per thread, double-buffered: round r+1 is in flight while
+  // round r is scanned.  Loads past the end return an all -inf vector, which
+  // never replaces a maximum.
+  constexpr int R = U * kArgThreads;   // vectors per round
+  constexpr uint32_t kNegInf = sizeof(T) == 2 ? 0xff80ff80u : 0xff800000u;
+  const int nround = (nvec + R - 1) / R;
+  auto load = [&](u32x4 (&x)[U], int r) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = ldg16(vb + (int64_t)(k + u * kArgThreads) * 16);
+    for (int u = 0; u < U; ++u) {
+      const int k = r * R + u * kArgThreads + (int)threadIdx.x;
+      x[u] = k < nvec ? ldg16_stream(vb + (int64_t)k * 16) : u32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    }
+  };
+  auto scan = [&](const u32x4 (&x)[U], int r) {
 #pragma unroll
     for (int u = 0; u < U; u += 2) {
-      scan16<T>(bv0, bi0, x[u], pre + (k + u * kArgThreads) * E);
-      scan16<T>(bv1, bi1, x[u + 1], pre + (k + (u + 1) * kArgThreads) * E);
+      scan16<T>(bv0, bi0, x[u], pre + (r * R + u * kArgThreads + (int)threadIdx.x) * E);
+      scan16<T>(bv1, bi1, x[u + 1], pre + (r * R + (u + 1) * kArgThreads + (int)threadIdx.x) * E);
     }
+  };
+  u32x4 xa[U], xb[U];
+  if (nround > 0) load(xa, 0);
+  int r = 0;
+  for (; r + 1 < nround; r += 2) {
+    load(xb, r + 1);
+    scan(xa, r);
+    if (r + 2 < nround) load(xa, r + 2);
+    scan(xb, r + 1);
   }
-  for (; k < nvec; k += kArgThreads) scan16<T>(bv0, bi0, ldg16(vb + (int64_t)k * 16), pre + k * E);
+  if (r < nround) scan(xa, r);
   for (int i = pre + nvec * E + threadIdx.x; i < V; i += kArgThreads) first_max(bv1, bi1, elem_at<T>(base, i), i);
   float bv = bv0;
   int bi = bi0;

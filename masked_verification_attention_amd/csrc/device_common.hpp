@@ -45,5 +45,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // 16-byte global load through the vector path.
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// 16-byte load of data read exactly once (streaming: no reuse in the caches)
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 }  // namespace sv
