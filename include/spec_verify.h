@@ -162,8 +162,8 @@ size_t spec_verify_attn_workspace(const spec_attn_desc* d);
  *            initialisation and are scratch after the call.
  *
  * Computation: fp32 accumulation; bf16 inputs use bf16 MFMA for QK^T and PV
- * (probabilities rounded to bf16 for PV) when (Hq/Hkv)*Tq >= 16, and fp32
- * VALU arithmetic otherwise.  Alignment: all tensors 16-byte aligned, and
+ * (probabilities rounded to bf16 for PV); fp32 inputs use fp32 VALU
+ * arithmetic throughout.  Alignment: all tensors 16-byte aligned, and
  * the strides a multiple of 16 bytes.
  * Limits: D in {64, 128}; 1 <= Tq <= 256; 0 <= S <= 256; B == 0 is a no-op.
  */

@@ -1,8 +1,6 @@
 // Masked verification attention on the vector ALUs.
 //
-// Used for fp32 inputs and for bf16 blocks whose rows per kv-head
-// ((Hq/Hkv) * Tq) are too few to fill a 16-row MFMA tile, e.g. Lookahead
-// Attention's k lookahead rows over a multi-head (non-grouped) cache.
+// Used for fp32 inputs (bf16 inputs always run on the matrix cores).
 //
 // Math ("Speculative Streaming", Equation 1): out = softmax(q k^T * scale) v
 // over the keys the row sees -- the soft prompt if its sp bit is set (ConFu
@@ -52,23 +50,6 @@ struct Elem<float> {
     x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
   }
 };
-template <>
-struct Elem<uint16_t> {
-  static constexpr int kSize = 2;
-  __device__ static float get(const void* p, int64_t i) {
-    return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
-  }
-  __device__ static void load8(const void* p, float* x) {
-    const u32x4 a = ldg16(p);
-    x[0] = bf16lo(a.x); x[1] = bf16hi(a.x); x[2] = bf16lo(a.y); x[3] = bf16hi(a.y);
-    x[4] = bf16lo(a.z); x[5] = bf16hi(a.z); x[6] = bf16lo(a.w); x[7] = bf16hi(a.w);
-  }
-  __device__ static void load4(const void* p, float* x) {
-    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-    x[0] = bf16lo(a.x); x[1] = bf16hi(a.x); x[2] = bf16lo(a.y); x[3] = bf16hi(a.y);
-  }
-};
-
 // Where the key with index t of this workgroup's key list lives.
 // List = prefix [ks, ke) ++ soft [0, ns) ++ block rows [0, nbk).
 struct KeyList {
@@ -337,13 +318,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, hipStream_t st) {
   const dim3 grid(a.n_split, a.B * a.Hkv);
   const dim3 block(kValuThreads);
-  if (dtype == SPEC_F32) {
-    if (a.D == 128) hipLaunchKernelGGL((k_attn_valu<float, 128>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_valu<float, 64>), grid, block, 0, st, a);
-  } else {
-    if (a.D == 128) hipLaunchKernelGGL((k_attn_valu<uint16_t, 128>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_valu<uint16_t, 64>), grid, block, 0, st, a);
-  }
+  if (dtype != SPEC_F32) return hipErrorInvalidValue;   // the planner sends bf16 to the MFMA kernel
+  if (a.D == 128) hipLaunchKernelGGL((k_attn_valu<float, 128>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_attn_valu<float, 64>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

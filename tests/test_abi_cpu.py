@@ -131,7 +131,16 @@ def test_other_entry_points_reject_bad_arguments():
 
 
 def test_workspace_policy():
-    # the tree/contemplate shape fills the chip without splitting; lookahead rows split ragged prefixes
+    # bf16 runs on the matrix cores and splits the prefix only when the (request, kv-head, row
+    # chunk) items cannot fill 256 CUs: the tree/contemplate shape and the 8-row lookahead shape
+    # over 32 heads both fill the chip unsplit
     assert bd.spec_verify_attn_workspace(good_desc(B=16)) == 0
     la = good_desc(B=8, Tq=8, Hq=32, Hkv=32, S=0, lmax=2056, strides=(2056 * 32 * 128, 32 * 128, 128))
-    assert bd.spec_verify_attn_workspace(la) > 0
+    assert bd.spec_verify_attn_workspace(la) == 0
+    # a single request over 8 kv-heads splits its long prefix (>= 512 keys per split)
+    one = good_desc(B=1, lmax=8192, strides=(8192 * 8 * 128, 8 * 128, 128))
+    assert bd.spec_verify_attn_workspace(one) > 0
+    # fp32 runs on the vector ALUs, which split every prefix into ~512-key pieces
+    la32 = good_desc(B=8, Tq=8, Hq=32, Hkv=32, S=0, lmax=2056, dtype=bd.SPEC_F32,
+                     strides=(2056 * 32 * 128, 32 * 128, 128))
+    assert bd.spec_verify_attn_workspace(la32) > 0
