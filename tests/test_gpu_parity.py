@@ -36,7 +36,7 @@ def oracle_attention(x, cfg, **kw):
                                    x["attn_parent"], x["sp_flag"], x["n_q"], cfg.dtype, **kw)
 
 
-def compare_attention(got, got_lse, ref, ref_lse, cfg, x, rows=None, requests=None):
+def compare_attention(got, got_lse, ref, ref_lse, cfg, x, rows=None, requests=None, atol=None):
     Bn, Tq = x["q"].shape[:2]
     reqs = range(Bn) if requests is None else requests
     worst, num, den = 0.0, 0.0, 0.0
@@ -57,7 +57,7 @@ def compare_attention(got, got_lse, ref, ref_lse, cfg, x, rows=None, requests=No
     rel = (num / den) ** 0.5 if den else 0.0
     say(f"    attention {cfg.name}: max-abs {worst:.3e}, rel-L2 {rel:.3e}")
     if cfg.dtype == "bf16":
-        assert worst <= BF16_ATOL
+        assert worst <= (BF16_ATOL if atol is None else atol)
         assert rel <= BF16_REL_L2
     else:
         assert worst <= F32_ATOL
@@ -78,6 +78,11 @@ SMALL_CASES = [
     ("c4_small", "c4_tree_3b", {"B": 2, "L": (200, 333)}, 0),
     ("c5_small", "c5_stream_70b", {"B": 1, "L": (257, 257)}, 0),
     ("c5_small_split", "c5_stream_70b", {"B": 1, "L": (257, 257)}, 2),
+    # long ragged prefixes (many steady-state steps), forced splits with ragged
+    # prefixes, ragged block rows
+    ("c3_long", "c3_confu_8b", {"B": 2, "L": (1500, 2047)}, 0),
+    ("c4_split3_ragged", "c4_tree_3b", {"B": 2, "L": (500, 1500)}, 3),
+    ("c3_ragged_nq", "c3_confu_8b", {"B": 3, "L": (700, 900), "n_q": np.array([60, 37, 1])}, 0),
 ]
 
 
@@ -99,6 +104,48 @@ def test_mask_and_attention_small(case):
     np.testing.assert_array_equal(sp, ref_sp)
     ref, ref_lse = oracle_attention(x, cfg)
     compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
+
+
+def test_mid_size_block_two_group_kernel():
+    # 15 nodes + 15 contemplate rows, GQA group 4: 120 rows per kv-head, the
+    # largest block that still runs two wave groups of 64-row slices
+    cfg = wl.CONFIGS["c3_confu_8b"].with_(T=15, name="c3_t15")
+    x = wl.generate(cfg, B=2, L=(400, 613), with_logits=False)
+    st = VerifyStep(cfg, x)
+    st.build_mask()
+    st.attention()
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_attention(x, cfg)
+    compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
+
+
+def test_large_scores_rescale_often():
+    # queries scaled by 6: scores spread over tens of log2 units, so the running
+    # max moves by more than the rescale threshold inside the steady-state steps
+    cfg = wl.CONFIGS["c3_confu_8b"].with_(name="c3_q6")
+    x = wl.generate(cfg, B=1, L=(2047, 2047), with_logits=False)
+    qf = (x["q"].astype(np.uint32) << 16).view(np.float32) * np.float32(6.0)
+    x["q"] = wl.f32_to_bf16_bits(qf)
+    st = VerifyStep(cfg, x)
+    st.build_mask()
+    st.attention()
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_attention(x, cfg)
+    # Out of the workloads' distribution, so not their 1e-2 bar: the kernels round
+    # the probabilities to bf16 (unit roundoff 2^-8) for the P*V product while
+    # normalising by their fp32 sum, which bounds a row's error by 2^-8 times the
+    # largest |v| it sees; peaky rows here are dominated by single V rows of
+    # magnitude ~4, so that bound, not 1e-2, is the one that holds.
+    vmax = max(np.abs(wl_values(x["v_cache"], cfg)).max(), np.abs(wl_values(x["v_blk"], cfg)).max(),
+               np.abs(wl_values(x["v_soft"], cfg)).max())
+    compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x, atol=2.0 ** -8 * vmax)
+
+
+def wl_values(a, cfg):
+    # stored inputs as float64 (bf16 bit patterns widened exactly), NaN canaries dropped
+    v = (a.astype(np.uint32) << 16).view(np.float32) if cfg.dtype == "bf16" else a
+    v = v.astype(np.float64)
+    return v[np.isfinite(v)]
 
 
 def test_d64_bf16_mfma_path():
