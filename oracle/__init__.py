@@ -18,7 +18,10 @@ the slow, obvious way (explicit dense masks, per-request loops, fp64):
 * ``acceptance`` -- per-node greedy target token (vocabulary argmax) and the
                     longest accepted root-to-node path found depth-first
                     (Speculative Streaming, the verification step;
-                    Lookahead Attention section 2.4).
+                    Lookahead Attention section 2.4); also with explicit
+                    verification rows, an explicit root and the correction
+                    token (the same verification step and the tree draft
+                    construction before it).
 * ``commit``     -- keep the accepted nodes' K/V in the cache, drop the rest
                     (Lookahead Attention section 3.2; Speculative Streaming,
                     tree pruning and its lazy garbage collection).
@@ -35,7 +38,7 @@ from .bf16 import bf16_bits_to_f64, as_f64
 from .mask import (ancestor_rows, block_visibility, soft_visibility, dense_visibility,
                    pack_bits, build_mask)
 from .attention import verify_attention
-from .acceptance import greedy_tokens, accept_request, argmax_accept
+from .acceptance import greedy_tokens, accept_request, argmax_accept, accept_request_rows, argmax_accept_rows
 from .commit import commit_kv
 
 __all__ = [
@@ -43,6 +46,6 @@ __all__ = [
     "ancestor_rows", "block_visibility", "soft_visibility", "dense_visibility",
     "pack_bits", "build_mask",
     "verify_attention",
-    "greedy_tokens", "accept_request", "argmax_accept",
+    "greedy_tokens", "accept_request", "argmax_accept", "accept_request_rows", "argmax_accept_rows",
     "commit_kv",
 ]

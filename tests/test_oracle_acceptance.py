@@ -169,3 +169,148 @@ def test_commit_invariants():
                 assert np.array_equal(v2[b, s], vb[b, path[b, d]])
             else:
                 assert np.array_equal(k2[b, s], kc[b, s]) and np.array_equal(v2[b, s], vc[b, s])
+
+
+# ---------------------------------------------------------------------------
+# Explicit verification rows, explicit root, correction token (the alignment of
+# a real model's verification pass: Speculative Streaming, the verification
+# step and tree draft construction).
+
+def rows_ok(draft, verify_row, greedy, n):
+    """Per-node match under explicit rows, written out independently."""
+    ok = np.zeros(n, dtype=bool)
+    for v in range(n):
+        u = int(verify_row[v])
+        if u == -1:
+            ok[v] = True
+        elif 0 <= u < n:
+            ok[v] = int(draft[v]) == int(greedy[u])
+    return ok
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_rows_match_brute_force_on_small_trees(seed):
+    rng = np.random.Generator(np.random.PCG64(500 + seed))
+    n = int(rng.integers(1, 9))
+    parent = wl.random_forest(rng, n, int(rng.integers(1, 5)))
+    greedy = rng.integers(0, 3, n).astype(np.int32)
+    draft = rng.integers(0, 3, n).astype(np.int32)
+    # rows: unchecked (-1), any row of the block, or out of range (never matches)
+    verify_row = rng.choice(np.array([-1, -2, n, n + 5] + list(range(n))), size=n).astype(np.int32)
+    max_depth = int(rng.integers(1, 6))
+    A, path, last, bonus = oracle.accept_request_rows(draft, parent, verify_row, greedy, n, max_depth)
+    bA, bpath = brute_force_accept(parent, rows_ok(draft, verify_row, greedy, n), max_depth)
+    assert A == bA
+    assert list(path[:A]) == bpath
+    assert (path[A:] == -1).all()
+    if A == 0:
+        assert last == -1 and bonus == -1
+    else:
+        assert last == bpath[-1] and bonus == greedy[bpath[-1]]
+
+
+def test_rows_identity_is_same_position_acceptance():
+    rng = np.random.Generator(np.random.PCG64(21))
+    B, T, V = 5, 12, 50
+    logits = rng.standard_normal((B, T, V)).astype(np.float32)
+    greedy = np.argmax(logits, axis=-1)
+    parent = np.stack([wl.random_forest(rng, T, 4) for _ in range(B)])
+    draft = np.where(rng.random((B, T)) < 0.7, greedy, rng.integers(0, V, (B, T))).astype(np.int32)
+    n_nodes = np.array([12, 7, 1, 12, 0], np.int32)
+    g1, A1, p1 = oracle.argmax_accept(logits, "f32", n_nodes, draft, parent, 6)
+    g2, A2, p2, last, bonus = oracle.argmax_accept_rows(logits, "f32", n_nodes, draft, parent, None, 6)
+    assert np.array_equal(g1, g2) and np.array_equal(A1, A2) and np.array_equal(p1, p2)
+    for b in range(B):
+        if A1[b]:
+            assert last[b] == p1[b, A1[b] - 1] and bonus[b] == g1[b, last[b]]
+        else:
+            assert last[b] == -1 and bonus[b] == -1
+
+
+@pytest.mark.parametrize("seed", range(50))
+def test_explicit_root_chain_closed_form(seed):
+    # chain 0 <- 1 <- ... <- k-1; node 0 is the root (the previous step's
+    # correction token, accepted unchecked); node v >= 1 is checked against the
+    # prediction of row v-1.  A = 1 + the leading run of matches, the step
+    # advances by A tokens and the correction token is row A-1's greedy token.
+    rng = np.random.Generator(np.random.PCG64(700 + seed))
+    k = int(rng.integers(1, 12))
+    parent = np.arange(-1, k - 1, dtype=np.int32)
+    verify_row = np.arange(-1, k - 1, dtype=np.int32)
+    greedy = rng.integers(0, 4, k).astype(np.int32)
+    hit = rng.random(k) < 0.7
+    draft = np.empty(k, np.int32)
+    draft[0] = 99
+    for v in range(1, k):
+        draft[v] = greedy[v - 1] if hit[v] else (greedy[v - 1] + 1) % 4
+    A, path, last, bonus = oracle.accept_request_rows(draft, parent, verify_row, greedy, k, k)
+    run = next((v for v in range(1, k) if not hit[v]), k) - 1
+    assert A == 1 + run
+    assert list(path[:A]) == list(range(A))
+    assert last == A - 1 and bonus == greedy[A - 1]
+
+
+def greedy_walk(parent, draft, greedy, root):
+    """Speculative Streaming's verification as a walk: from the root, step to
+    the child whose drafted token is the greedy prediction of the current
+    node's row (siblings carry distinct tokens, so it is unique) until none is."""
+    path = [root]
+    while True:
+        u = path[-1]
+        nxt = [c for c in range(len(parent)) if parent[c] == u and draft[c] == greedy[u]]
+        assert len(nxt) <= 1
+        if not nxt:
+            return path
+        path.append(nxt[0])
+
+
+@pytest.mark.parametrize("seed", range(100))
+def test_parent_rows_equal_the_greedy_walk(seed):
+    # a tree of the real-model layout: node 0 is the root, every other node's
+    # parent precedes it, siblings carry distinct tokens, and node v is
+    # verified by its parent's row
+    rng = np.random.Generator(np.random.PCG64(900 + seed))
+    n = int(rng.integers(1, 20))
+    parent = np.full(n, -1, np.int32)
+    for v in range(1, n):
+        parent[v] = int(rng.integers(0, v))
+    V = 30
+    draft = np.zeros(n, np.int32)
+    for u in range(-1, n):
+        kids = [c for c in range(n) if parent[c] == u]
+        toks = rng.choice(V, size=len(kids), replace=False)
+        for c, t in zip(kids, toks):
+            draft[c] = t
+    # each row's greedy token: one of its children's tokens w.p. 0.7, else a fresh token
+    greedy = np.zeros(n, np.int32)
+    for u in range(n):
+        kids = [c for c in range(n) if parent[c] == u]
+        if kids and rng.random() < 0.7:
+            greedy[u] = draft[kids[int(rng.integers(0, len(kids)))]]
+        else:
+            greedy[u] = V + int(rng.integers(0, 5))
+    verify_row = np.where(parent < 0, -1, parent).astype(np.int32)
+    walk = greedy_walk(parent, draft, greedy, 0)
+    A, path, last, bonus = oracle.accept_request_rows(draft, parent, verify_row, greedy, n, 16)
+    assert A == min(len(walk), 16)
+    assert list(path[:A]) == walk[:A]
+    assert bonus == greedy[walk[A - 1]]
+
+
+def test_rows_out_of_range_and_unchecked():
+    parent = np.array([-1, 0, 1, 0], np.int32)
+    greedy = np.array([5, 6, 7, 8], np.int32)
+    draft = np.array([0, 5, 6, 5], np.int32)
+    # every node unchecked: everything accepted, A = tree depth, DFS-first deepest path
+    A, path, last, bonus = oracle.accept_request_rows(draft, parent, np.full(4, -1, np.int32), greedy, 4, 8)
+    assert A == 3 and list(path[:3]) == [0, 1, 2] and bonus == 7
+    # a row past n_nodes, or below -1, never matches
+    A, path, _, bonus = oracle.accept_request_rows(draft, parent, np.array([-1, 0, 4, -3], np.int32), greedy, 4, 8)
+    assert A == 2 and list(path[:2]) == [0, 1] and bonus == 6
+    # rows past n_nodes carry no greedy token in the batch form
+    logits = np.zeros((1, 4, 10), np.float32)
+    for v, g in enumerate([5, 6, 7, 8]):
+        logits[0, v, g] = 1.0
+    _, A, path, _, bonus = oracle.argmax_accept_rows(logits, "f32", np.array([2], np.int32), draft[None],
+                                                     parent[None], np.array([[-1, 0, 1, 0]], np.int32), 8)
+    assert A[0] == 2 and list(path[0, :2]) == [0, 1] and bonus[0] == 6
