@@ -12,6 +12,8 @@
  *   spec_verify_attn    attention of the block's queries over
  *                       [soft prompt | cached prefix | block] under that mask
  *   spec_argmax_accept  per-node greedy token, longest accepted path
+ *   spec_argmax_accept_rows  the same with explicit verification rows, an
+ *                       explicit root and the correction token
  *   spec_commit_kv      append the accepted nodes' K/V to the cache
  *
  * Sources (page titles; sections, equations):
@@ -203,6 +205,45 @@ int spec_argmax_accept(const void* logits, int32_t logits_dtype, int32_t B, int3
                        const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
                        int32_t max_depth, int32_t* out_argmax, int32_t* out_len,
                        int32_t* out_path, void* stream);
+
+/*
+ * spec_argmax_accept_rows -- greedy verification with explicit verification
+ * rows: the alignment of a real model's verification pass.
+ *
+ * In [SS]'s verification step the walk starts at the root, the previous
+ * step's correction token, which is part of the flattened tree ([SS] tree
+ * draft construction, step 2); the target's output at a node's position is
+ * its prediction for the NEXT token, so a drafted node is checked against
+ * its parent's row; and at the point where the walk stops the target's logits
+ * give one correction token, so the step advances by the accepted drafts plus
+ * one.  [CF] likewise hands the last accepted node's own output (its future
+ * prediction) to the next round.  This call takes that alignment as data:
+ * For node v < n_nodes[b]:
+ *   out_argmax[b][v] as in spec_argmax_accept (row v's greedy token)
+ *   u = verify_row[b][v]
+ *   match(v) = (u == -1)            node v is accepted unchecked (an explicit,
+ *                                   already accepted root)
+ *           or (0 <= u < n_nodes[b] and draft_tok[b][v] == out_argmax[b][u]);
+ *              any other u never matches
+ *   accepted, depth, out_len, out_path exactly as in spec_argmax_accept
+ *   out_bonus[b] = out_argmax[b][out_path[b][out_len[b] - 1]], the greedy
+ *                  token of the last accepted node's row (the correction
+ *                  token); -1 when out_len[b] == 0.
+ * With the root in the block (verify_row -1, parent -1) and every other node
+ * verified by its parent's row, out_len[b] = beta + 1 counts the root: the
+ * path is exactly the set of rows whose K/V spec_commit_kv appends, and the
+ * step advances by out_len[b] tokens (beta drafts + the correction token).
+ * verify_row == NULL means verify_row[b][v] = v, i.e. spec_argmax_accept;
+ * out_bonus may be NULL.
+ *
+ *   verify_row [B, T] int32 or NULL; out_bonus [B] int32 out or NULL;
+ *   every other argument as in spec_argmax_accept.
+ * Limits and errors as in spec_argmax_accept.
+ */
+int spec_argmax_accept_rows(const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,
+                            const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
+                            const int32_t* verify_row, int32_t max_depth, int32_t* out_argmax,
+                            int32_t* out_len, int32_t* out_path, int32_t* out_bonus, void* stream);
 
 /*
  * spec_commit_kv -- keep the accepted tokens' K/V ([SS] lazy garbage

@@ -32,7 +32,7 @@ SPEC_MAX_SOFT = 256
 
 # every symbol the header declares
 EXPORTS = ("spec_build_mask", "spec_verify_attn_workspace", "spec_verify_attn", "spec_argmax_accept",
-           "spec_commit_kv", "spec_strerror", "spec_last_error", "spec_version")
+           "spec_argmax_accept_rows", "spec_commit_kv", "spec_strerror", "spec_last_error", "spec_version")
 
 
 class SpecError(RuntimeError):
@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_attn.restype = ctypes.c_int
     lib.spec_argmax_accept.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P]
     lib.spec_argmax_accept.restype = ctypes.c_int
+    lib.spec_argmax_accept_rows.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]
+    lib.spec_argmax_accept_rows.restype = ctypes.c_int
     lib.spec_commit_kv.argtypes = [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P, _P, _I, _P]
     lib.spec_commit_kv.restype = ctypes.c_int
     lib.spec_strerror.argtypes = [ctypes.c_int]
@@ -137,6 +139,16 @@ def spec_argmax_accept(logits, logits_dtype, B, T, V, n_nodes, draft_tok, acc_pa
                                   _ptr(acc_parent), max_depth, _ptr(out_argmax), _ptr(out_len),
                                   _ptr(out_path), _stream(stream) if B else None),
            "spec_argmax_accept")
+
+
+def spec_argmax_accept_rows(logits, logits_dtype, B, T, V, n_nodes, draft_tok, acc_parent, verify_row,
+                            max_depth, out_argmax, out_len, out_path, out_bonus, stream=None):
+    lib = load()
+    _check(lib.spec_argmax_accept_rows(_ptr(logits), logits_dtype, B, T, V, _ptr(n_nodes), _ptr(draft_tok),
+                                       _ptr(acc_parent), _ptr(verify_row), max_depth, _ptr(out_argmax),
+                                       _ptr(out_len), _ptr(out_path), _ptr(out_bonus),
+                                       _stream(stream) if B else None),
+           "spec_argmax_accept_rows")
 
 
 def spec_commit_kv(desc: AttnDesc, k_cache, v_cache, cache_len_in, cache_len_out, k_blk, v_blk, out_len,

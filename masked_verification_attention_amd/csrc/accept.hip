@@ -9,16 +9,22 @@
 // value, then lower index", so ties resolve to the lowest index and -0
 // compares equal to +0.
 //
-// k_accept: one workgroup per request, one thread per node.  Each thread
+// k_accept: one workgroup per request, one thread per node.  A node matches
+// when its draft equals the greedy token of its verification row -- its own
+// row, or a given row (a real model checks a child against its parent's
+// prediction; row -1 accepts an explicit root unchecked).  Each thread
 // walks its node's path to the root: the node is accepted iff every node on
-// the path matches its draft and the path is no longer than max_depth.  The
+// the path matches and the path is no longer than max_depth.  The
 // accepted length is the largest accepted depth ("Speculative Streaming":
 // the longest accepted path; "Lookahead Attention" 2.4: the longest
 // consistent prefix of a chain).  Among the deepest accepted nodes the path a
 // depth-first walk meets first (children in increasing index) is the one
 // with the lexicographically smallest root-first index sequence; node indices
 // are < 256 and paths are <= 16 long, so a path packs into a 128-bit key
-// (8 bits per depth, root in the top byte) and a min-reduction finds it.
+// (8 bits per depth, root in the top byte) and a min-reduction finds it.  The
+// correction token is the greedy token of the path's last node's row
+// ("Speculative Streaming", the verification step: one token from the
+// target's logits where the walk stopped).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -153,9 +159,11 @@ __device__ __forceinline__ bool key_less(uint64_t ah, uint64_t al, uint64_t bh, 
 __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* __restrict__ n_nodes,
                                                         const int32_t* __restrict__ draft_tok,
                                                         const int32_t* __restrict__ acc_parent,
+                                                        const int32_t* __restrict__ verify_row,
                                                         const int32_t* __restrict__ argmax, int max_depth,
                                                         int32_t* __restrict__ out_len,
-                                                        int32_t* __restrict__ out_path) {
+                                                        int32_t* __restrict__ out_path,
+                                                        int32_t* __restrict__ out_bonus) {
   __shared__ int32_t par[SPEC_MAX_NODES];
   __shared__ uint8_t okv[SPEC_MAX_NODES];
   __shared__ int red_i[kAccThreads / kWave];
@@ -169,7 +177,11 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
   const int lane = v % kWave;
   if (v < n) {
     par[v] = acc_parent[(int64_t)b * T_ + v];
-    okv[v] = draft_tok[(int64_t)b * T_ + v] == argmax[(int64_t)b * T_ + v] ? 1 : 0;
+    // the row whose greedy token verifies node v: v itself, or the given row
+    // (-1 = accepted unchecked; a row outside [0, n) never matches)
+    const int u = verify_row ? verify_row[(int64_t)b * T_ + v] : v;
+    okv[v] = u == -1 ? 1
+                     : ((u >= 0 && u < n && draft_tok[(int64_t)b * T_ + v] == argmax[(int64_t)b * T_ + u]) ? 1 : 0);
   }
   __syncthreads();
 
@@ -242,6 +254,17 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
   if (v == 0) {
     red_h[0] = kh;
     red_l[0] = kl;
+    if (out_bonus != nullptr) {
+      // correction token: the greedy token of the last accepted node's row
+      int bonus = -1;
+      if (a_len > 0) {
+        const int d = a_len - 1;
+        const uint64_t w = d < 8 ? kh : kl;
+        const int last = (int)((w >> (56 - 8 * (d & 7))) & 0xffull);
+        bonus = argmax[(int64_t)b * T_ + last];
+      }
+      out_bonus[b] = bonus;
+    }
   }
   __syncthreads();
   if (v < max_depth) {
@@ -268,10 +291,11 @@ hipError_t launch_argmax(const void* logits, int dtype, int B, int T, int V, con
 }
 
 hipError_t launch_accept(int B, int T, const int32_t* n_nodes, const int32_t* draft_tok,
-                         const int32_t* acc_parent, const int32_t* argmax, int max_depth,
-                         int32_t* out_len, int32_t* out_path, hipStream_t st) {
-  hipLaunchKernelGGL(k_accept, dim3(B), dim3(kAccThreads), 0, st, T, n_nodes, draft_tok, acc_parent, argmax,
-                     max_depth, out_len, out_path);
+                         const int32_t* acc_parent, const int32_t* verify_row, const int32_t* argmax,
+                         int max_depth, int32_t* out_len, int32_t* out_path, int32_t* out_bonus,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(k_accept, dim3(B), dim3(kAccThreads), 0, st, T, n_nodes, draft_tok, acc_parent, verify_row,
+                     argmax, max_depth, out_len, out_path, out_bonus);
   return hipGetLastError();
 }
 

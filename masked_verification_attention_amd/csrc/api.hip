@@ -121,6 +121,38 @@ AttnPlan plan_attn(const spec_attn_desc& d) {
 
 }  // namespace sv
 
+namespace {
+
+int argmax_accept_impl(const char* fn, const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,
+                       const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
+                       const int32_t* verify_row, int32_t max_depth, int32_t* out_argmax, int32_t* out_len,
+                       int32_t* out_path, int32_t* out_bonus, void* stream) {
+  REQUIRE(B >= 0, SPEC_EINVAL, "%s: B = %d < 0", fn, B);
+  REQUIRE(T >= 1 && T <= SPEC_MAX_NODES, SPEC_EINVAL, "%s: T = %d outside [1, %d]", fn, T, SPEC_MAX_NODES);
+  REQUIRE(V >= 1, SPEC_EINVAL, "%s: V = %d < 1", fn, V);
+  REQUIRE(max_depth >= 1 && max_depth <= SPEC_MAX_DEPTH, SPEC_EINVAL, "%s: max_depth = %d outside [1, %d]", fn,
+          max_depth, SPEC_MAX_DEPTH);
+  REQUIRE(logits_dtype == SPEC_F32 || logits_dtype == SPEC_BF16, SPEC_EINVAL,
+          "%s: logits_dtype = %d is not a spec_dtype", fn, logits_dtype);
+  REQUIRE((int64_t)B * T <= 0x7fffffff, SPEC_EUNSUPPORTED, "%s: B * T too large", fn);
+  if (B == 0) return ok();
+  REQUIRE(logits && n_nodes && draft_tok && acc_parent && out_argmax && out_len && out_path, SPEC_EINVAL,
+          "%s: logits, n_nodes, draft_tok, acc_parent and the outputs argmax, len, path must be non-NULL", fn);
+  REQUIRE(aligned(logits, esize_of(logits_dtype)), SPEC_EINVAL, "%s: logits must be aligned to its element size",
+          fn);
+  REQUIRE(aligned(n_nodes, 4) && aligned(draft_tok, 4) && aligned(acc_parent, 4) && aligned(verify_row, 4) &&
+              aligned(out_argmax, 4) && aligned(out_len, 4) && aligned(out_path, 4) && aligned(out_bonus, 4),
+          SPEC_EINVAL, "%s: int32 arrays must be 4-byte aligned", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = sv::launch_argmax(logits, logits_dtype, B, T, V, n_nodes, out_argmax, s);
+  if (e != hipSuccess) return hip_status(e, "argmax launch");
+  e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, verify_row, out_argmax, max_depth, out_len,
+                        out_path, out_bonus, s);
+  return hip_status(e, "acceptance scan launch");
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* spec_version(void) { return "0.1.0"; }
@@ -239,26 +271,16 @@ int spec_argmax_accept(const void* logits, int32_t logits_dtype, int32_t B, int3
                        const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
                        int32_t max_depth, int32_t* out_argmax, int32_t* out_len, int32_t* out_path,
                        void* stream) {
-  REQUIRE(B >= 0, SPEC_EINVAL, "B = %d < 0", B);
-  REQUIRE(T >= 1 && T <= SPEC_MAX_NODES, SPEC_EINVAL, "T = %d outside [1, %d]", T, SPEC_MAX_NODES);
-  REQUIRE(V >= 1, SPEC_EINVAL, "V = %d < 1", V);
-  REQUIRE(max_depth >= 1 && max_depth <= SPEC_MAX_DEPTH, SPEC_EINVAL, "max_depth = %d outside [1, %d]",
-          max_depth, SPEC_MAX_DEPTH);
-  REQUIRE(logits_dtype == SPEC_F32 || logits_dtype == SPEC_BF16, SPEC_EINVAL,
-          "logits_dtype = %d is not a spec_dtype", logits_dtype);
-  REQUIRE((int64_t)B * T <= 0x7fffffff, SPEC_EUNSUPPORTED, "B * T too large");
-  if (B == 0) return ok();
-  REQUIRE(logits && n_nodes && draft_tok && acc_parent && out_argmax && out_len && out_path, SPEC_EINVAL,
-          "all array arguments must be non-NULL");
-  REQUIRE(aligned(logits, esize_of(logits_dtype)), SPEC_EINVAL, "logits must be aligned to its element size");
-  REQUIRE(aligned(n_nodes, 4) && aligned(draft_tok, 4) && aligned(acc_parent, 4) && aligned(out_argmax, 4) &&
-              aligned(out_len, 4) && aligned(out_path, 4),
-          SPEC_EINVAL, "int32 arrays must be 4-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = sv::launch_argmax(logits, logits_dtype, B, T, V, n_nodes, out_argmax, s);
-  if (e != hipSuccess) return hip_status(e, "spec_argmax_accept argmax launch");
-  e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, out_argmax, max_depth, out_len, out_path, s);
-  return hip_status(e, "spec_argmax_accept scan launch");
+  return argmax_accept_impl("spec_argmax_accept", logits, logits_dtype, B, T, V, n_nodes, draft_tok, acc_parent,
+                            nullptr, max_depth, out_argmax, out_len, out_path, nullptr, stream);
+}
+
+int spec_argmax_accept_rows(const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,
+                            const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
+                            const int32_t* verify_row, int32_t max_depth, int32_t* out_argmax, int32_t* out_len,
+                            int32_t* out_path, int32_t* out_bonus, void* stream) {
+  return argmax_accept_impl("spec_argmax_accept_rows", logits, logits_dtype, B, T, V, n_nodes, draft_tok,
+                            acc_parent, verify_row, max_depth, out_argmax, out_len, out_path, out_bonus, stream);
 }
 
 int spec_commit_kv(const spec_attn_desc* d, void* k_cache, void* v_cache, const int32_t* cache_len_in,

@@ -121,6 +121,14 @@ def test_other_entry_points_reject_bad_arguments():
         lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, 17, FAKE, FAKE, FAKE, stream=0),
         lambda: bd.spec_argmax_accept(FAKE, 3, 2, 4, 100, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, stream=0),
         lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, None, FAKE, 4, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept_rows(FAKE, bd.SPEC_BF16, 2, 0, 100, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE,
+                                           FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept_rows(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, None, FAKE, 4, FAKE, FAKE,
+                                           FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept_rows(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, FAKE + 2, 4, FAKE,
+                                           FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept_rows(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, FAKE, 17, FAKE, FAKE,
+                                           FAKE, FAKE, stream=0),
         lambda: bd.spec_commit_kv(good_desc(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0),
         lambda: bd.spec_commit_kv(good_desc(), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, stream=0),
         lambda: bd.spec_commit_kv(good_desc(D=80), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, stream=0),
