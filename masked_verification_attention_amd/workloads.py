@@ -18,6 +18,10 @@ Workload shapes follow the three pages this library implements:
 * Speculative Streaming (SS), "Speculative Streaming: Fast LLM Inference
   without Auxiliary Models", tree draft and Equation 4: each node sees its
   ancestors; several candidate streams that are causal within themselves.
+  Its multi-stream form ("msa_tree"): the tree draft of top-k tokens per
+  speculative stream -- a complete k-ary tree of depth gamma, 1 + sum k^g
+  nodes, flattened level by level -- with every node carrying its main stream
+  and gamma speculative streams (Equation 2 and the batching paragraph).
 
 Value recipe: float32 standard normal draws, rounded to bfloat16 with
 round-to-nearest-even (bf16 tensors are returned as their uint16 bit
@@ -58,7 +62,7 @@ class VerifyConfig:
     dtype: str                  # "f32" or "bf16" for q, k, v, soft prompt
     L: Tuple[int, int]          # prefix length range, inclusive (lo == hi: fixed)
     S: int                      # soft-prompt KV rows (0 = none)
-    structure: str              # "la_cache", "la_full", "confu_tree", "stream_chains"
+    structure: str              # "la_cache", "la_full", "confu_tree", "stream_chains", "msa_tree"
     T: int                      # acceptance nodes per request
     V: int                      # vocabulary size
     logits_dtype: str           # "f32" or "bf16"
@@ -67,6 +71,8 @@ class VerifyConfig:
     depth_cap: int = 6          # tree depth cap (confu_tree)
     chain_len: int = 4          # nodes per chain (stream_chains)
     n_lookahead: int = 0        # la_full: k lookahead rows after the n = L[0] originals
+    gamma: int = 0              # msa_tree: speculative streams per node (tree depth)
+    branch: int = 0             # msa_tree: tokens drawn per stream position (children per node)
     seed: int = 1000
 
     @property
@@ -80,6 +86,8 @@ class VerifyConfig:
             return 2 * self.T
         if self.structure == "la_full":
             return self.L[0] + self.n_lookahead
+        if self.structure == "msa_tree":
+            return (1 + self.gamma) * self.T
         return self.T
 
     @property
@@ -89,6 +97,8 @@ class VerifyConfig:
             return self.depth_cap
         if self.structure == "stream_chains":
             return self.chain_len
+        if self.structure == "msa_tree":
+            return self.gamma + 1          # the root (accepted unchecked) and gamma levels
         return self.T
 
     def with_(self, **kw) -> "VerifyConfig":
@@ -118,6 +128,16 @@ CONFIGS: Dict[str, VerifyConfig] = {
         structure="stream_chains", T=128, V=128256, logits_dtype="bf16", accept_p=0.75,
         chain_len=4, seed=1004),
 }
+
+# Speculative Streaming's multi-stream verification (the tree-draft ablation of
+# its Figure 5: gamma = 3, k = 3 unpruned, 40 nodes, 160 MSA rows) on an
+# OPT-1.3B-shaped layer (32 heads of 64, no GQA, 50272-token vocabulary); the
+# prefix lengths are a reading (the page's tasks have prompts of a few hundred
+# tokens).
+CONFIGS["c6_msa_1b"] = VerifyConfig(
+    name="c6_msa_1b", B=8, Hq=32, Hkv=32, D=64, dtype="bf16", L=(256, 1024), S=0,
+    structure="msa_tree", T=40, V=50272, logits_dtype="bf16", accept_p=0.8,
+    gamma=3, branch=3, seed=1006)
 
 # The full form of the tiny LA workload: the n = 128 original tokens are part of
 # the block as a causal chain and the k = 4 lookahead rows hang off the last one,
@@ -172,8 +192,22 @@ def chain_forest(n_chains: int, chain_len: int) -> np.ndarray:
     return parent
 
 
+def kary_tree(branch: int, gamma: int) -> np.ndarray:
+    """Complete branch-ary tree of depth gamma, flattened level by level.
+
+    Node 0 is the root; the children of node p are branch*p + 1 .. branch*p +
+    branch, so parents precede children.  1 + sum_{g=1..gamma} branch^g nodes.
+    """
+    n = sum(branch ** g for g in range(gamma + 1))
+    parent = np.full(n, -1, dtype=np.int32)
+    for v in range(1, n):
+        parent[v] = (v - 1) // branch
+    return parent
+
+
 def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] = None,
              L: Optional[Tuple[int, int]] = None, n_q: Optional[np.ndarray] = None,
+             n_nodes: Optional[np.ndarray] = None,
              with_logits: bool = True) -> Dict[str, np.ndarray]:
     """Draw one full set of inputs for ``cfg``.
 
@@ -181,7 +215,9 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
     k_soft, v_soft, logits, accept coins, random tokens.  ``B`` and ``L``
     override the batch and the prefix range (smaller parity cases);
     ``n_q`` overrides the valid query rows per request (ragged padding tests;
-    padded rows are the last Tq - n_q rows).
+    padded rows are the last Tq - n_q rows).  For "msa_tree", ``n_nodes``
+    keeps only the first n_nodes[b] tree nodes of request b (a pruned tree;
+    its n_nodes[b] * (1 + gamma) rows are valid) and ``n_q`` is not accepted.
     """
     if B is not None:
         cfg = cfg.with_(B=B)
@@ -203,7 +239,25 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
     sp_flag = np.zeros((Bn, Tq), dtype=np.uint8)
     acc_parent = np.full((Bn, T), -1, dtype=np.int32)
     node_row = np.arange(T, dtype=np.int32)  # block row of node v
+    tree_parent = None
+    if cfg.structure == "msa_tree":
+        if n_q is not None:
+            raise ValueError("msa_tree takes n_nodes, not n_q")
+        tree = kary_tree(cfg.branch, cfg.gamma)
+        if len(tree) != T:
+            raise ValueError(f"T = {T} but a complete {cfg.branch}-ary tree of depth {cfg.gamma} "
+                             f"has {len(tree)} nodes")
+        tree_parent = np.tile(tree, (Bn, 1))
+        acc_parent[:] = tree_parent
+        nn = np.full(Bn, T, dtype=np.int32) if n_nodes is None else np.asarray(n_nodes, dtype=np.int32)
+        if nn.shape != (Bn,) or nn.min() < 0 or nn.max() > T:
+            raise ValueError("n_nodes out of range")
+        n_q = nn * (1 + cfg.gamma)
+    elif n_nodes is not None:
+        raise ValueError("n_nodes is only taken by msa_tree")
     for b in range(Bn):
+        if cfg.structure == "msa_tree":
+            continue
         if cfg.structure == "la_cache":
             acc_parent[b] = np.arange(-1, T - 1, dtype=np.int32)
         elif cfg.structure == "la_full":
@@ -228,7 +282,10 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
     if n_q is None:
         n_q = np.full(Bn, Tq, dtype=np.int32)
     n_q = np.asarray(n_q, dtype=np.int32)
-    n_nodes = np.full(Bn, T, dtype=np.int32)
+    if cfg.structure == "msa_tree":
+        n_nodes = (n_q // (1 + cfg.gamma)).astype(np.int32)
+    else:
+        n_nodes = np.full(Bn, T, dtype=np.int32)
     if cfg.structure in ("la_cache", "stream_chains"):
         n_nodes = np.minimum(n_nodes, n_q).astype(np.int32)
 
@@ -255,6 +312,8 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
         q=q, k_cache=k_cache, v_cache=v_cache, k_blk=k_blk, v_blk=v_blk,
         k_soft=k_soft, v_soft=v_soft,
     )
+    if tree_parent is not None:
+        out["tree_parent"] = tree_parent
 
     # -- logits and drafts
     if with_logits:
@@ -272,7 +331,13 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
                    if cfg.logits_dtype == "bf16" else np.float32(PLANTED_LOGIT))
         for b in range(Bn):
             for v in range(T):
-                if coins[b, v]:
+                if not coins[b, v]:
+                    continue
+                if cfg.structure == "msa_tree":
+                    # a node is checked against its parent's main-stream output
+                    if tree_parent[b, v] >= 0:
+                        logits[b, tree_parent[b, v], tokens[b, v]] = planted
+                else:
                     logits[b, v, tokens[b, v]] = planted
         out.update(logits=logits, draft_tok=tokens, planted=coins)
     return out

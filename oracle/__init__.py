@@ -25,6 +25,9 @@ the slow, obvious way (explicit dense masks, per-request loops, fp64):
 * ``commit``     -- keep the accepted nodes' K/V in the cache, drop the rest
                     (Lookahead Attention section 3.2; Speculative Streaming,
                     tree pruning and its lazy garbage collection).
+* ``msa``        -- the multi-stream rows of a tree draft and what each sees
+                    (Speculative Streaming, Equations 1, 2 and 4, and its
+                    batching with speculative streams).
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against things
 other than itself -- the 7x7 mask drawn on the Lookahead Attention page (after
@@ -40,6 +43,7 @@ from .mask import (ancestor_rows, block_visibility, soft_visibility, dense_visib
 from .attention import verify_attention
 from .acceptance import greedy_tokens, accept_request, argmax_accept, accept_request_rows, argmax_accept_rows
 from .commit import commit_kv
+from .msa import msa_row, tree_path, msa_block_visibility, build_msa_mask
 
 __all__ = [
     "bf16_bits_to_f64", "as_f64",
@@ -48,4 +52,5 @@ __all__ = [
     "verify_attention",
     "greedy_tokens", "accept_request", "argmax_accept", "accept_request_rows", "argmax_accept_rows",
     "commit_kv",
+    "msa_row", "tree_path", "msa_block_visibility", "build_msa_mask",
 ]

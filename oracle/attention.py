@@ -24,11 +24,14 @@ from .mask import dense_visibility
 def verify_attention(q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft,
                      attn_parent, sp_flag, n_q, dtype: str, scale: Optional[float] = None,
                      requests: Optional[Sequence[int]] = None,
-                     rows: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                     rows: Optional[Sequence[int]] = None,
+                     block_vis=None) -> Tuple[np.ndarray, np.ndarray]:
     """Return (out [B, Tq, Hq, D], lse [B, Tq, Hq]) in float64.
 
     ``requests`` / ``rows`` restrict the computation to a subset (entries
     not computed are NaN), for sampled checks of large workloads.
+    ``block_vis`` (bool [B, Tq, Tq]) gives the block keys each row sees in
+    place of ``attn_parent`` (multi-stream rows, ``msa.msa_block_visibility``).
     """
     B, Tq, Hq, D = q.shape
     Hkv = k_cache.shape[2]
@@ -46,7 +49,8 @@ def verify_attention(q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_sof
         L = int(cache_len[b])
         nq = int(n_q[b])
         sp_row = None if sp_flag is None else sp_flag[b]
-        M = dense_visibility(attn_parent[b], sp_row, nq, S, L)        # [Tq, S+L+Tq]
+        M = dense_visibility(None if attn_parent is None else attn_parent[b], sp_row, nq, S, L,
+                             None if block_vis is None else block_vis[b])   # [Tq, S+L+Tq]
         M = M[:, : S + L + nq]                                        # drop padded block keys
         K = np.concatenate([soft_k, as_f64(k_cache[b, :L], dtype), as_f64(k_blk[b, :nq], dtype)])
         V = np.concatenate([soft_v, as_f64(v_cache[b, :L], dtype), as_f64(v_blk[b, :nq], dtype)])

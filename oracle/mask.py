@@ -60,18 +60,21 @@ def soft_visibility(sp_flag_row: np.ndarray, n_q: int, Tq: int) -> np.ndarray:
     return s
 
 
-def dense_visibility(attn_parent_row, sp_flag_row, n_q: int, S: int, L: int) -> np.ndarray:
+def dense_visibility(attn_parent_row, sp_flag_row, n_q: int, S: int, L: int,
+                     block=None) -> np.ndarray:
     """Dense bool [Tq, S + L + Tq] over keys ordered [soft | prefix | block].
 
     ConFu places the soft prompt before the input in the cache dimension; the
-    order of keys does not change the attention result.
+    order of keys does not change the attention result.  ``block`` (bool
+    [Tq, Tq]) replaces the parent-array rule for the block keys (the
+    multi-stream rows of ``msa``).
     """
-    Tq = len(attn_parent_row)
+    Tq = len(attn_parent_row) if block is None else block.shape[0]
     M = np.zeros((Tq, S + L + Tq), dtype=bool)
     valid = np.arange(Tq) < n_q
     M[:, :S] = soft_visibility(sp_flag_row, n_q, Tq)[:, None] & (S > 0)
     M[:, S:S + L] = valid[:, None]
-    M[:, S + L:] = block_visibility(attn_parent_row, n_q, Tq)
+    M[:, S + L:] = block_visibility(attn_parent_row, n_q, Tq) if block is None else block
     return M
 
 
