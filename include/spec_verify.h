@@ -130,6 +130,44 @@ int spec_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag, const in
                     void* stream);
 
 /*
+ * spec_build_msa_mask -- block masks for multi-stream (MSA) verification rows.
+ *
+ * [SS] Multi-Stream Attention: every node of the flattened tree draft carries
+ * one main-stream query and gamma speculative-stream queries (the batching
+ * paragraph: (1 + gamma) rows per tree node).  Row layout of request b with
+ * n = n_nodes[b] nodes: rows 0..n-1 are the main streams of nodes 0..n-1,
+ * row n + v*gamma + (j-1) is speculative stream j (1..gamma) of node v, and
+ * rows from n*(1+gamma) on are padding.  What each row sees (Equations 1 and
+ * 2 over the tree of Equation 4, read through its prose):
+ *   main stream of v      the main rows of the nodes on the root-to-v path
+ *                         (v included), never another branch;
+ *   stream j of v         the same main rows plus streams 1..j of v itself,
+ *                         never another node's streams.
+ * Every valid row also sees the whole cached prefix; no row sees the soft
+ * prompt (sp_bits is all zero).  The main rows of nodes are the first n rows,
+ * so a node's parent index is also the row of its parent's main stream: pass
+ * tree_parent as verify_row to spec_argmax_accept_rows (root: -1, accepted
+ * unchecked), and the accepted path's node indices are the main rows to
+ * commit (stream K/V is never committed).
+ *
+ *   tree_parent [B, N] int32    parent node, -1 = the root.  Precondition:
+ *                               -1 <= tree_parent[b][v] < v; a link that
+ *                               breaks it ends the walk.
+ *   n_nodes     [B] int32       tree nodes per request, clamped to [0, N].
+ *   gamma                       speculative streams per node, >= 0.
+ *   Tq                          rows of the block, >= N * (1 + gamma).
+ *   mask_bits   [B, Tq, W] uint32 out, W = ceil(Tq/32), as spec_build_mask.
+ *   sp_bits     [B, W] uint32   out: all zero.
+ *   n_q         [B] int32       out: valid rows n_nodes[b] * (1 + gamma), the
+ *                               n_q argument of spec_verify_attn.
+ *
+ * Limits: 1 <= N, N * (1 + gamma) <= Tq <= 256.  B == 0 is a no-op.
+ */
+int spec_build_msa_mask(const int32_t* tree_parent, const int32_t* n_nodes, int32_t B, int32_t N,
+                        int32_t gamma, int32_t Tq, uint32_t* mask_bits, uint32_t* sp_bits, int32_t* n_q,
+                        void* stream);
+
+/*
  * spec_verify_attn_workspace -- bytes of device workspace spec_verify_attn
  * needs for this descriptor (0 if none).  Returns 0 for an invalid
  * descriptor as well; spec_verify_attn reports the error.

@@ -31,7 +31,8 @@ SPEC_MAX_DEPTH = 16
 SPEC_MAX_SOFT = 256
 
 # every symbol the header declares
-EXPORTS = ("spec_build_mask", "spec_verify_attn_workspace", "spec_verify_attn", "spec_argmax_accept",
+EXPORTS = ("spec_build_mask", "spec_build_msa_mask", "spec_verify_attn_workspace", "spec_verify_attn",
+           "spec_argmax_accept",
            "spec_argmax_accept_rows", "spec_commit_kv", "spec_strerror", "spec_last_error", "spec_version")
 
 
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     lib.spec_build_mask.argtypes = [_P, _P, _P, _I, _I, _P, _P, _P]
     lib.spec_build_mask.restype = ctypes.c_int
+    lib.spec_build_msa_mask.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
+    lib.spec_build_msa_mask.restype = ctypes.c_int
     lib.spec_verify_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc)]
     lib.spec_verify_attn_workspace.restype = ctypes.c_size_t
     lib.spec_verify_attn.argtypes = [ctypes.POINTER(AttnDesc)] + [_P] * 14 + [ctypes.c_size_t, _P]
@@ -115,6 +118,13 @@ def spec_build_mask(attn_parent, sp_flag, n_q, B, Tq, mask_bits, sp_bits, stream
     lib = load()
     _check(lib.spec_build_mask(_ptr(attn_parent), _ptr(sp_flag), _ptr(n_q), B, Tq, _ptr(mask_bits),
                                _ptr(sp_bits), _stream(stream) if B else None), "spec_build_mask")
+
+
+def spec_build_msa_mask(tree_parent, n_nodes, B, N, gamma, Tq, mask_bits, sp_bits, n_q, stream=None):
+    lib = load()
+    _check(lib.spec_build_msa_mask(_ptr(tree_parent), _ptr(n_nodes), B, N, gamma, Tq, _ptr(mask_bits),
+                                   _ptr(sp_bits), _ptr(n_q), _stream(stream) if B else None),
+           "spec_build_msa_mask")
 
 
 def spec_verify_attn_workspace(desc: AttnDesc) -> int:

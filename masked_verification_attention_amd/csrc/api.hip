@@ -184,6 +184,26 @@ int spec_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag, const in
                     "spec_build_mask launch");
 }
 
+int spec_build_msa_mask(const int32_t* tree_parent, const int32_t* n_nodes, int32_t B, int32_t N,
+                        int32_t gamma, int32_t Tq, uint32_t* mask_bits, uint32_t* sp_bits, int32_t* n_q,
+                        void* stream) {
+  REQUIRE(B >= 0, SPEC_EINVAL, "B = %d < 0", B);
+  REQUIRE(gamma >= 0 && gamma < SPEC_MAX_TQ, SPEC_EINVAL, "gamma = %d outside [0, %d)", gamma, SPEC_MAX_TQ);
+  REQUIRE(N >= 1 && N <= SPEC_MAX_TQ, SPEC_EINVAL, "N = %d outside [1, %d]", N, SPEC_MAX_TQ);
+  REQUIRE(Tq >= 1 && Tq <= SPEC_MAX_TQ, SPEC_EINVAL, "Tq = %d outside [1, %d]", Tq, SPEC_MAX_TQ);
+  REQUIRE((int64_t)N * (1 + gamma) <= Tq, SPEC_EINVAL, "N * (1 + gamma) = %lld rows exceed Tq = %d",
+          (long long)N * (1 + gamma), Tq);
+  if (B == 0) return ok();
+  REQUIRE(tree_parent && n_nodes && mask_bits && sp_bits && n_q, SPEC_EINVAL,
+          "tree_parent, n_nodes, mask_bits, sp_bits and n_q must be non-NULL");
+  REQUIRE(aligned(tree_parent, 4) && aligned(n_nodes, 4) && aligned(mask_bits, 4) && aligned(sp_bits, 4) &&
+              aligned(n_q, 4),
+          SPEC_EINVAL, "int32/uint32 arrays must be 4-byte aligned");
+  return hip_status(sv::launch_build_msa_mask(tree_parent, n_nodes, B, N, gamma, Tq, mask_bits, sp_bits, n_q,
+                                              static_cast<hipStream_t>(stream)),
+                    "spec_build_msa_mask launch");
+}
+
 size_t spec_verify_attn_workspace(const spec_attn_desc* d) {
   if (check_desc(d) != SPEC_OK) return 0;
   return sv::plan_attn(*d).ws_bytes;

@@ -54,6 +54,9 @@ AttnPlan plan_attn(const spec_attn_desc& d);
 
 hipError_t launch_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag, const int32_t* n_q,
                              int B, int Tq, uint32_t* mask_bits, uint32_t* sp_bits, hipStream_t st);
+hipError_t launch_build_msa_mask(const int32_t* tree_parent, const int32_t* n_nodes, int B, int N,
+                                 int gamma, int Tq, uint32_t* mask_bits, uint32_t* sp_bits,
+                                 int32_t* n_q, hipStream_t st);
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);

@@ -2,7 +2,8 @@
 
 Uploads one seeded workload (``workloads.generate``) to HBM as torch tensors,
 allocates every output, and runs the four entry points on one stream:
-spec_build_mask -> spec_verify_attn -> spec_argmax_accept -> spec_commit_kv.
+spec_build_mask -> spec_verify_attn -> spec_argmax_accept -> spec_commit_kv
+(multi-stream workloads: spec_build_msa_mask and spec_argmax_accept_rows).
 This module only moves memory and marshals arguments; all arithmetic runs in
 the HIP kernels.  torch supplies the device memory and the stream.
 """
@@ -81,6 +82,10 @@ class VerifyStep:
         self.draft_tok = to_device(x["draft_tok"], "i32", dev) if "draft_tok" in x else None
         self.logits = to_device(x["logits"], cfg.logits_dtype, dev) if "logits" in x else None
         self.V = x["logits"].shape[2] if "logits" in x else cfg.V
+        # multi-stream rows: the mask comes from the tree, and a node is verified by its
+        # parent's main-stream row (main rows are the first rows of the block)
+        self.msa = cfg.structure == "msa_tree"
+        self.tree_parent = to_device(x["tree_parent"], "i32", dev) if self.msa else None
 
         i32 = dict(dtype=torch.int32, device=dev)
         self.mask_bits = torch.zeros(self.B, self.Tq, self.W, **i32)
@@ -90,6 +95,7 @@ class VerifyStep:
         self.argmax = torch.empty(self.B, self.T, **i32)
         self.out_len = torch.empty(self.B, **i32)
         self.out_path = torch.empty(self.B, self.max_depth, **i32)
+        self.out_bonus = torch.empty(self.B, **i32)
         self.cache_len_out = torch.empty(self.B, **i32)
 
         Hkv, D = cfg.Hkv, cfg.D
@@ -110,6 +116,10 @@ class VerifyStep:
 
     # -- the four entry points
     def build_mask(self, stream=None):
+        if self.msa:
+            bd.spec_build_msa_mask(self.tree_parent, self.n_nodes, self.B, self.T, self.cfg.gamma, self.Tq,
+                                   self.mask_bits, self.sp_bits, self.n_q, stream)
+            return
         bd.spec_build_mask(self.attn_parent, self.sp_flag, self.n_q, self.B, self.Tq, self.mask_bits,
                            self.sp_bits, stream)
 
@@ -121,6 +131,12 @@ class VerifyStep:
                             self.workspace, self.ws_bytes, stream)
 
     def argmax_accept(self, stream=None):
+        if self.msa:
+            bd.spec_argmax_accept_rows(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.T, self.V,
+                                       self.n_nodes, self.draft_tok, self.acc_parent, self.tree_parent,
+                                       self.max_depth, self.argmax, self.out_len, self.out_path,
+                                       self.out_bonus, stream)
+            return
         bd.spec_argmax_accept(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.T, self.V,
                               self.n_nodes, self.draft_tok, self.acc_parent, self.max_depth, self.argmax,
                               self.out_len, self.out_path, stream)

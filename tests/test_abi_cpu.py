@@ -107,6 +107,7 @@ def test_verify_attn_rejects_bad_pointers_and_workspace():
 def test_empty_batch_is_a_noop_without_touching_memory():
     attn(good_desc(B=0), q=None, out=None)
     bd.spec_build_mask(None, None, None, 0, 8, None, None, stream=0)
+    bd.spec_build_msa_mask(None, None, 0, 40, 3, 160, None, None, None, stream=0)
     bd.spec_argmax_accept(None, bd.SPEC_BF16, 0, 4, 100, None, None, None, 4, None, None, None, stream=0)
     bd.spec_commit_kv(good_desc(B=0), None, None, None, None, None, None, None, None, 4, stream=0)
 
@@ -116,6 +117,13 @@ def test_other_entry_points_reject_bad_arguments():
         lambda: bd.spec_build_mask(FAKE, None, FAKE, 2, 0, FAKE, FAKE, stream=0),
         lambda: bd.spec_build_mask(FAKE, None, FAKE, 2, 300, FAKE, FAKE, stream=0),
         lambda: bd.spec_build_mask(None, None, FAKE, 2, 8, FAKE, FAKE, stream=0),
+        lambda: bd.spec_build_msa_mask(FAKE, FAKE, 2, 40, 3, 159, FAKE, FAKE, FAKE, stream=0),   # rows > Tq
+        lambda: bd.spec_build_msa_mask(FAKE, FAKE, 2, 0, 3, 160, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_build_msa_mask(FAKE, FAKE, 2, 40, -1, 160, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_build_msa_mask(FAKE, FAKE, 2, 2, 200, 257, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_build_msa_mask(FAKE, FAKE, 2, 40, 3, 160, FAKE, FAKE, None, stream=0),
+        lambda: bd.spec_build_msa_mask(FAKE, FAKE + 1, 2, 40, 3, 160, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_build_msa_mask(FAKE, FAKE, -1, 40, 3, 160, FAKE, FAKE, FAKE, stream=0),
         lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 0, 100, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, stream=0),
         lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 4, 0, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, stream=0),
         lambda: bd.spec_argmax_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, 17, FAKE, FAKE, FAKE, stream=0),

@@ -1,0 +1,229 @@
+"""GPU parity of multi-stream (MSA) verification through the C ABI.
+
+Speculative Streaming's verification pass with Multi-Stream Attention: every
+tree node carries its main stream and gamma speculative streams.  The HIP
+path builds the block mask from the tree (spec_build_msa_mask), runs the
+same verify attention, accepts with the parent's main-stream row verifying
+each node (spec_argmax_accept_rows) and commits main-stream rows only.  The
+oracle side takes its visibility from Equations 1 and 2 written out
+(oracle.msa_block_visibility), its verification rows from its own row
+layout, and its attention, acceptance and commit from the same pinned
+functions as the other workloads.
+
+Bars as for the other workloads: bit-exact masks, row counts, argmax,
+acceptance and commit; attention within max-abs 1e-2 (bf16) and relative L2
+1e-2; bitwise invariance of main-stream outputs under changes of the
+speculative rows' K/V (which no main stream may see).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from masked_verification_attention_amd import binding as bd
+from masked_verification_attention_amd import workloads as wl
+from masked_verification_attention_amd.step import VerifyStep
+
+pytestmark = pytest.mark.gpu
+
+BF16_ATOL = 1e-2
+BF16_REL_L2 = 1e-2
+LSE_ATOL = 2e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def random_tree(rng, n):
+    par = np.full(n, -1, dtype=np.int32)
+    for v in range(1, n):
+        par[v] = int(rng.integers(0, v))
+    return par
+
+
+def oracle_vis(x, cfg):
+    B = x["q"].shape[0]
+    return np.stack([oracle.msa_block_visibility(x["tree_parent"][b], int(x["n_nodes"][b]), cfg.gamma, cfg.Tq)
+                     for b in range(B)])
+
+
+def oracle_attention(x, cfg, **kw):
+    return oracle.verify_attention(x["q"], x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"],
+                                   None, None, None, None, x["n_q"], cfg.dtype, block_vis=oracle_vis(x, cfg),
+                                   **kw)
+
+
+def oracle_accept(x, cfg, max_depth):
+    B, T = x["tree_parent"].shape
+    vrow = np.full((B, T), -1, dtype=np.int32)
+    for b in range(B):
+        n = int(x["n_nodes"][b])
+        for v in range(n):
+            p = int(x["tree_parent"][b, v])
+            vrow[b, v] = -1 if p < 0 else oracle.msa_row(n, cfg.gamma, p, 0)
+    return oracle.argmax_accept_rows(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                     x["acc_parent"], vrow, max_depth)
+
+
+def compare_attention(got, got_lse, ref, ref_lse, cfg, x, rows=None, requests=None):
+    Bn, Tq = x["q"].shape[:2]
+    worst, num, den = 0.0, 0.0, 0.0
+    for b in (range(Bn) if requests is None else requests):
+        nq = int(x["n_q"][b])
+        for r in (range(Tq) if rows is None else rows):
+            if r >= nq:
+                assert (got[b, r] == 0).all(), f"padded row {b},{r} not zero"
+                assert np.isneginf(got_lse[b, r]).all()
+                continue
+            g, e = got[b, r].astype(np.float64), ref[b, r]
+            assert np.isfinite(g).all(), f"non-finite output at {b},{r}"
+            worst = max(worst, float(np.abs(g - e).max()))
+            num += float(((g - e) ** 2).sum())
+            den += float((e ** 2).sum())
+            np.testing.assert_allclose(got_lse[b, r], ref_lse[b, r], rtol=0, atol=LSE_ATOL)
+    rel = (num / den) ** 0.5 if den else 0.0
+    say(f"    attention {cfg.name}: max-abs {worst:.3e}, rel-L2 {rel:.3e}")
+    assert worst <= BF16_ATOL
+    assert rel <= BF16_REL_L2
+
+
+MASK_CASES = [
+    # (N nodes, gamma, Tq, n_nodes per request)
+    (3, 2, 9, [3, 2, 1, 0]),
+    (40, 3, 160, [40, 13, 1]),
+    (31, 4, 155, [31, 30]),
+    (15, 3, 64, [15, 7]),            # spare padding rows past N * (1 + gamma)
+    (32, 7, 256, [32, 5]),           # the largest block
+    (256, 0, 256, [256, 100]),       # no streams: the plain tree rule
+    (1, 0, 1, [1, 0]),
+    (1, 255, 256, [1]),              # one node, the most streams
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[f"N{c[0]}_g{c[1]}_T{c[2]}" for c in MASK_CASES])
+def test_msa_mask_random_trees(case):
+    N, gamma, Tq, nn = case
+    rng = np.random.default_rng(N * 1000 + gamma * 10 + Tq)
+    B = len(nn)
+    tree = np.stack([random_tree(rng, N) for _ in range(B)])
+    n_nodes = np.array(nn, dtype=np.int32)
+    W = (Tq + 31) // 32
+    dev = dict(dtype=torch.int32, device="cuda")
+    t_tree = torch.from_numpy(tree).cuda()
+    t_nn = torch.from_numpy(n_nodes).cuda()
+    bits = torch.full((B, Tq, W), -1, **dev)       # stale contents must be overwritten
+    sp = torch.full((B, W), -1, **dev)
+    nq = torch.full((B,), -7, **dev)
+    say(f"[gpu] msa mask N={N} gamma={gamma} Tq={Tq}")
+    bd.spec_build_msa_mask(t_tree, t_nn, B, N, gamma, Tq, bits, sp, nq)
+    torch.cuda.synchronize()
+    ref_bits, ref_sp, ref_nq = oracle.build_msa_mask(tree, n_nodes, gamma, Tq)
+    np.testing.assert_array_equal(bits.cpu().numpy().view(np.uint32), ref_bits)
+    np.testing.assert_array_equal(sp.cpu().numpy().view(np.uint32), ref_sp)
+    np.testing.assert_array_equal(nq.cpu().numpy(), ref_nq)
+
+
+SMALL = [
+    # (id, config overrides, generate overrides)
+    ("c6_small", {}, {"B": 2, "L": (100, 300)}),
+    ("c6_pruned", {}, {"B": 3, "L": (64, 200), "n_nodes": np.array([40, 13, 1])}),
+    ("c6_g4k2", {"gamma": 4, "branch": 2, "T": 31}, {"B": 2, "L": (150, 260)}),
+    ("c6_g3k2", {"gamma": 3, "branch": 2, "T": 15}, {"B": 2, "L": (90, 90)}),
+    ("c6_d128_gqa", {"Hq": 32, "Hkv": 8, "D": 128}, {"B": 2, "L": (200, 333)}),
+    ("c6_empty_prefix", {}, {"B": 2, "L": (0, 0)}),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_msa_step_small(case):
+    cid, cov, gov = case
+    cfg = wl.CONFIGS["c6_msa_1b"].with_(name=cid, **cov)
+    say(f"[gpu] {cid}: generate")
+    x = wl.generate(cfg, **gov)
+    st = VerifyStep(cfg, x)
+    st.n_q.fill_(-1)                                # the mask call must write the row counts
+    say(f"[gpu] {cid}: step (Tq {st.Tq}, ws {st.ws_bytes} B)")
+    st.run()
+    torch.cuda.synchronize()
+    ref_bits, ref_sp, ref_nq = oracle.build_msa_mask(x["tree_parent"], x["n_nodes"], cfg.gamma, cfg.Tq)
+    np.testing.assert_array_equal(st.mask_bits.cpu().numpy().view(np.uint32), ref_bits)
+    np.testing.assert_array_equal(st.n_q.cpu().numpy(), ref_nq)
+    ref, ref_lse = oracle_attention(x, cfg)
+    compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
+    greedy, A, path, last, bonus = oracle_accept(x, cfg, st.max_depth)
+    got_am = st.argmax.cpu().numpy()
+    for b in range(x["q"].shape[0]):
+        n = int(x["n_nodes"][b])
+        np.testing.assert_array_equal(got_am[b, :n], greedy[b, :n])
+    np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
+    np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
+    np.testing.assert_array_equal(st.out_bonus.cpu().numpy(), bonus)
+    # the accepted nodes' main-stream rows are what is committed
+    rows = np.full_like(path, -1)
+    for b in range(path.shape[0]):
+        for d in range(int(A[b])):
+            rows[b, d] = oracle.msa_row(int(x["n_nodes"][b]), cfg.gamma, int(path[b, d]), 0)
+    kc, vc, L2 = oracle.commit_kv(x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"], A, rows)
+    np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L2)
+    k_host, v_host = st.cache_host()
+    np.testing.assert_array_equal(k_host, kc)
+    np.testing.assert_array_equal(v_host, vc)
+    say(f"    accepted lengths {A.tolist()}, bonus {bonus.tolist()}")
+
+
+def test_main_streams_ignore_stream_rows_bitwise():
+    cfg = wl.CONFIGS["c6_msa_1b"]
+    x = wl.generate(cfg, B=2, L=(120, 180), with_logits=False)
+    st = VerifyStep(cfg, x)
+    st.build_mask()
+    st.attention()
+    torch.cuda.synchronize()
+    base = st.out.clone()
+    T = cfg.T
+    g = torch.Generator(device="cuda").manual_seed(3)
+    # speculative rows' K/V: no main stream may see them
+    st.k_blk[:, T:] = torch.randn(st.k_blk[:, T:].shape, generator=g, device="cuda").to(torch.bfloat16)
+    st.v_blk[:, T:] = torch.randn(st.v_blk[:, T:].shape, generator=g, device="cuda").to(torch.bfloat16)
+    st.attention()
+    torch.cuda.synchronize()
+    assert torch.equal(st.out[:, :T], base[:, :T])
+    assert not torch.equal(st.out[:, T:], base[:, T:])
+
+
+def test_msa_full_size_sampled():
+    """The multi-stream workload at full size in the benchmark's launch configuration
+    (head-major cache, automatic split); attention on sampled rows (main and stream rows
+    of first, middle and last nodes), everything else everywhere."""
+    cfg = wl.CONFIGS["c6_msa_1b"]
+    reqs, rows = [0, 3, 7], [0, 1, 20, 39, 40, 42, 100, 159]
+    say("[gpu] full-size c6_msa_1b: generate")
+    x = wl.generate(cfg)
+    st = VerifyStep(cfg, x, layout="bhld")
+    say(f"[gpu] full-size c6_msa_1b: run step (ws {st.ws_bytes} B)")
+    st.run()
+    torch.cuda.synchronize()
+    ref_bits, _, ref_nq = oracle.build_msa_mask(x["tree_parent"], x["n_nodes"], cfg.gamma, cfg.Tq)
+    np.testing.assert_array_equal(st.mask_bits.cpu().numpy().view(np.uint32), ref_bits)
+    np.testing.assert_array_equal(st.n_q.cpu().numpy(), ref_nq)
+    say("[gpu] full-size c6_msa_1b: oracle on sampled rows")
+    ref, ref_lse = oracle_attention(x, cfg, requests=reqs, rows=rows)
+    compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x, rows=rows,
+                      requests=reqs)
+    assert np.isfinite(st.out.cpu().numpy()).all()
+    greedy, A, path, last, bonus = oracle_accept(x, cfg, st.max_depth)
+    np.testing.assert_array_equal(st.argmax.cpu().numpy(), greedy)
+    np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
+    np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
+    np.testing.assert_array_equal(st.out_bonus.cpu().numpy(), bonus)
+    L = x["cache_len"]
+    np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L + A)
+    k_host, _ = st.cache_host()
+    for b in range(cfg.B):
+        for d in range(int(A[b])):
+            np.testing.assert_array_equal(k_host[b, L[b] + d], x["k_blk"][b, path[b, d]])
+    say(f"    accepted lengths {A.tolist()}")
