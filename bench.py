@@ -5,10 +5,15 @@ Llama-3-8B workload (16 requests, 32 query / 8 kv heads, head dim 128, bf16,
 4096-token prefix + 16 soft-prompt rows, 30-node draft tree + 30 contemplate
 rows = 60 query rows per request, 128256-entry vocabulary):
     spec_build_mask -> spec_verify_attn -> spec_argmax_accept -> spec_commit_kv
-Inputs are resident in HBM before timing starts; three independent input
-sets (~1.3 GB) are cycled so that the 256 MB last-level cache cannot hold a
-step's working set.  The metric is speculative query tokens verified per
-second (sum of valid block rows / step time).
+Inputs are resident in HBM before timing starts; independent input sets
+(at least three and ~1 GB in all: 1.3 GB for this workload) are cycled so
+that the 256 MB last-level cache cannot hold a step's working set.  The
+metric is speculative query tokens verified per second (sum of valid block
+rows / step time).
+
+--workload c6_msa_1b times Speculative Streaming's multi-stream verification
+instead (spec_build_msa_mask -> spec_verify_attn -> spec_argmax_accept_rows ->
+spec_commit_kv on a 40-node tree with 3 speculative streams per node).
 
 The K/V cache is laid out head-major, [B, Hkv, lmax, D] (each kv-head's keys
 contiguous), which the library takes through the descriptor's strides
@@ -44,8 +49,16 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
-WORKLOAD = "c3_confu_8b"
+WORKLOAD = "c3_confu_8b"        # the headline workload (default)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_mfma_c3_counters.json")
+# workloads bench.py can time (the headline one and the multi-stream tree draft)
+DESCRIPTIONS = {
+    "c3_confu_8b": ("ConFu-shaped Llama-3-8B verify: batch 16, 32q/8kv heads, head_dim 128, prefix 4096 + "
+                    "16 soft rows, 30-node tree + 30 contemplate rows, vocab 128256", 4096),
+    "c6_msa_1b": ("Speculative Streaming multi-stream verify, OPT-1.3B-shaped: batch 8, 32 heads, head_dim 64, "
+                  "prefix U{256..1024}, 40-node tree (gamma 3, k 3) x (1 + 3 streams) = 160 rows, vocab 50272",
+                  1024),
+}
 ATTN_SRC = os.path.join(ROOT, "masked_verification_attention_amd", "csrc", "attn_mfma.hip")
 
 
@@ -72,6 +85,16 @@ def attention_flops(cfg, x) -> int:
     """4*D flops per visible (query head, key) pair; visible pairs counted from the inputs."""
     B, Tq = x["q"].shape[:2]
     total = 0
+    if cfg.structure == "msa_tree":
+        # main stream of node v: prefix + its path; stream j: also streams 1..j of v
+        for b in range(B):
+            L = int(x["cache_len"][b])
+            for v in range(int(x["n_nodes"][b])):
+                depth, p = 1, int(x["tree_parent"][b, v])
+                while p >= 0:
+                    depth, p = depth + 1, int(x["tree_parent"][b, p])
+                total += sum(L + depth + j for j in range(cfg.gamma + 1)) * cfg.Hq
+        return total * 4 * cfg.D
     for b in range(B):
         L = int(x["cache_len"][b])
         nq = int(x["n_q"][b])
@@ -136,42 +159,54 @@ def summarize_pmc(d: str):
     print(json.dumps(rec, indent=1))
 
 
-def counters_traffic():
+def counters_traffic(workload: str):
     """HBM bytes per attention launch from committed rocprofv3 counter runs, or None
     if the kernel source changed since they were taken."""
     try:
         with open(COUNTERS_FILE) as f:
             rec = json.load(f)
         sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if rec.get("kernel_src_sha256") != sha:
+        if rec.get("kernel_src_sha256") != sha or rec.get("workload") != workload:
             return None
         return rec.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         return None
 
 
-def cpu_baseline(requests: int):
+def cpu_baseline(workload: str, requests: int):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     from threadpoolctl import threadpool_limits
 
     import oracle
     from masked_verification_attention_amd import workloads as wl
 
-    cfg = wl.CONFIGS[WORKLOAD]
+    cfg = wl.CONFIGS[workload]
+    requests = min(requests, cfg.B)
     x = wl.generate(cfg, B=requests)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.build_mask(x["attn_parent"], x["sp_flag"], x["n_q"])
-        oracle.verify_attention(x["q"], x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"],
-                                x["k_soft"], x["v_soft"], x["attn_parent"], x["sp_flag"], x["n_q"], cfg.dtype)
-        _, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
-                                          x["acc_parent"], cfg.max_depth)
+        if cfg.structure == "msa_tree":
+            oracle.build_msa_mask(x["tree_parent"], x["n_nodes"], cfg.gamma, cfg.Tq)
+            vis = np.stack([oracle.msa_block_visibility(x["tree_parent"][b], int(x["n_nodes"][b]), cfg.gamma,
+                                                        cfg.Tq) for b in range(requests)])
+            oracle.verify_attention(x["q"], x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"],
+                                    None, None, None, None, x["n_q"], cfg.dtype, block_vis=vis)
+            vrow = np.array([[-1 if p < 0 else oracle.msa_row(int(x["n_nodes"][b]), cfg.gamma, int(p), 0)
+                              for p in x["tree_parent"][b]] for b in range(requests)], dtype=np.int32)
+            _, A, path, _, _ = oracle.argmax_accept_rows(x["logits"], cfg.logits_dtype, x["n_nodes"],
+                                                         x["draft_tok"], x["acc_parent"], vrow, cfg.max_depth)
+        else:
+            oracle.build_mask(x["attn_parent"], x["sp_flag"], x["n_q"])
+            oracle.verify_attention(x["q"], x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"],
+                                    x["k_soft"], x["v_soft"], x["attn_parent"], x["sp_flag"], x["n_q"], cfg.dtype)
+            _, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                              x["acc_parent"], cfg.max_depth)
         oracle.commit_kv(x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"], A, path)
         dt = time.perf_counter() - t0
     tokens = int(x["n_q"].sum())
     return {"value": tokens / dt, "unit": "spec query tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{requests} of the 16 requests of the workload ({tokens} query tokens, full "
-                      f"4096-token prefix), whole step (mask, attention, argmax+acceptance, commit), "
+            "sample": f"{requests} of the {cfg.B} requests of the workload ({tokens} query tokens, full "
+                      f"prefixes), whole step (mask, attention, argmax+acceptance, commit), "
                       f"fp64 numpy, BLAS limited to 1 thread; {dt:.1f} s"}
 
 
@@ -180,7 +215,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sets", type=int, default=3, help="input sets cycled between steps")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets cycled between steps (0: enough for ~1 GB, at least 3)")
+    ap.add_argument("--workload", choices=sorted(DESCRIPTIONS), default=WORKLOAD)
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0)
@@ -207,11 +244,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    cfg = wl.CONFIGS[WORKLOAD]
+    cfg = wl.CONFIGS[args.workload]
     steps_state = []
     t0 = time.time()
+    first = wl.generate(cfg, seed=cfg.seed)
+    if args.sets <= 0:
+        args.sets = int(min(16, max(3, np.ceil(1e9 / wl.nbytes_of(first)))))
     for i in range(args.sets):
-        x = wl.generate(cfg, seed=cfg.seed + 100 * i)
+        x = first if i == 0 else wl.generate(cfg, seed=cfg.seed + 100 * i)
         st = VerifyStep(cfg, x, device="cuda:0", kv_splits=args.kv_splits, layout=args.layout)
         steps_state.append((st, x))
     torch.cuda.synchronize()
@@ -273,17 +313,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "ConFu-shaped Llama-3-8B verify: batch 16, 32q/8kv heads, head_dim 128, "
-                               "prefix 4096 + 16 soft rows, 30-node tree + 30 contemplate rows, vocab 128256",
-                   "global_batch": cfg.B, "seq_len": 4096, "query_rows": cfg.Tq, "kv_layout": args.layout,
+        "config": {"workload": DESCRIPTIONS[args.workload][0],
+                   "global_batch": cfg.B, "seq_len": DESCRIPTIONS[args.workload][1], "query_rows": cfg.Tq,
+                   "kv_layout": args.layout,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": counters_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counters_traffic(args.workload),
                      "kernel": "k_attn_mfma", "algorithmic_bytes_per_launch": alg_bytes,
                      "mean_launch_us": attn_mean, "tflops": tflops},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_requests)
+        result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_requests)
         log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s ({result['cpu_baseline']['sample']})")
     print(json.dumps(result), flush=True)
 
