@@ -84,7 +84,10 @@ AttnPlan plan_attn(const spec_attn_desc& d) {
   // padded to 16-row tiles, streams the cache ~3x faster than the VALU kernel
   if (d.dtype == SPEC_BF16) {
     p.path = PATH_MFMA;
-    p.rows_per_wg = R > 64 ? 128 : 64;
+    // 128-row workgroups share each K/V tile between more rows, but at head
+    // dim 64 the 64-row workgroup (half the LDS ring, under 128 registers a
+    // lane) lets two workgroups share a CU, which measured faster
+    p.rows_per_wg = (R > 64 && d.D == 128) ? 128 : 64;
     p.row_chunks = (R + p.rows_per_wg - 1) / p.rows_per_wg;
     const int64_t items = items_bh * p.row_chunks;
     int n = 1;
