@@ -191,8 +191,10 @@ def cpu_baseline(workload: str, requests: int):
                                                         cfg.Tq) for b in range(requests)])
             oracle.verify_attention(x["q"], x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"],
                                     None, None, None, None, x["n_q"], cfg.dtype, block_vis=vis)
-            vrow = np.array([[-1 if p < 0 else oracle.msa_row(int(x["n_nodes"][b]), cfg.gamma, int(p), 0)
-                              for p in x["tree_parent"][b]] for b in range(requests)], dtype=np.int32)
+            vrow = np.full(x["acc_parent"].shape, -1, dtype=np.int32)
+            for b in range(requests):
+                for v, p in enumerate(x["tree_parent"][b]):
+                    vrow[b, v] = -1 if p < 0 else oracle.msa_row(int(x["n_nodes"][b]), cfg.gamma, int(p), 0)
             _, A, path, _, _ = oracle.argmax_accept_rows(x["logits"], cfg.logits_dtype, x["n_nodes"],
                                                          x["draft_tok"], x["acc_parent"], vrow, cfg.max_depth)
         else:

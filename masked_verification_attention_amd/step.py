@@ -117,7 +117,8 @@ class VerifyStep:
     # -- the four entry points
     def build_mask(self, stream=None):
         if self.msa:
-            bd.spec_build_msa_mask(self.tree_parent, self.n_nodes, self.B, self.T, self.cfg.gamma, self.Tq,
+            bd.spec_build_msa_mask(self.tree_parent, self.n_nodes, self.B, self.tree_parent.shape[1],
+                                   self.cfg.gamma, self.Tq,
                                    self.mask_bits, self.sp_bits, self.n_q, stream)
             return
         bd.spec_build_mask(self.attn_parent, self.sp_flag, self.n_q, self.B, self.Tq, self.mask_bits,

@@ -237,7 +237,11 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
     # -- structure
     attn_parent = np.full((Bn, Tq), -1, dtype=np.int32)
     sp_flag = np.zeros((Bn, Tq), dtype=np.uint8)
-    acc_parent = np.full((Bn, T), -1, dtype=np.int32)
+    # acceptance arrays and logit rows: one per node; for msa_tree one per block
+    # row (the LM head runs over every row: main rows verify, the speculative
+    # rows of the last accepted node draft the next tree) with the nodes first
+    Ta = Tq if cfg.structure == "msa_tree" else T
+    acc_parent = np.full((Bn, Ta), -1, dtype=np.int32)
     node_row = np.arange(T, dtype=np.int32)  # block row of node v
     tree_parent = None
     if cfg.structure == "msa_tree":
@@ -248,7 +252,7 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
             raise ValueError(f"T = {T} but a complete {cfg.branch}-ary tree of depth {cfg.gamma} "
                              f"has {len(tree)} nodes")
         tree_parent = np.tile(tree, (Bn, 1))
-        acc_parent[:] = tree_parent
+        acc_parent[:, :T] = tree_parent
         nn = np.full(Bn, T, dtype=np.int32) if n_nodes is None else np.asarray(n_nodes, dtype=np.int32)
         if nn.shape != (Bn,) or nn.min() < 0 or nn.max() > T:
             raise ValueError("n_nodes out of range")
@@ -318,7 +322,7 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
     # -- logits and drafts
     if with_logits:
         V = cfg.V
-        logits = _values(rng, (Bn, T, V), cfg.logits_dtype)
+        logits = _values(rng, (Bn, Ta, V), cfg.logits_dtype)
         if cfg.exact_accepts is not None:
             coins = np.zeros((Bn, T), dtype=bool)
             for b in range(Bn):
@@ -326,7 +330,8 @@ def generate(cfg: VerifyConfig, seed: Optional[int] = None, *, B: Optional[int] 
                 coins[b, pick] = True
         else:
             coins = rng.random(size=(Bn, T)) < cfg.accept_p
-        tokens = rng.integers(0, V, size=(Bn, T), dtype=np.int64).astype(np.int32)
+        tokens = np.zeros((Bn, Ta), dtype=np.int32)
+        tokens[:, :T] = rng.integers(0, V, size=(Bn, T), dtype=np.int64).astype(np.int32)
         planted = (f32_to_bf16_bits(np.array([PLANTED_LOGIT], np.float32))[0]
                    if cfg.logits_dtype == "bf16" else np.float32(PLANTED_LOGIT))
         for b in range(Bn):

@@ -28,6 +28,10 @@ the slow, obvious way (explicit dense masks, per-request loops, fp64):
 * ``msa``        -- the multi-stream rows of a tree draft and what each sees
                     (Speculative Streaming, Equations 1, 2 and 4, and its
                     batching with speculative streams).
+* ``draft``      -- the next tree draft: per-stream top-k tokens of the last
+                    accepted node's streams, linked stream to stream under the
+                    correction token (Speculative Streaming, tree draft
+                    construction and parallel new draft generation).
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against things
 other than itself -- the 7x7 mask drawn on the Lookahead Attention page (after
@@ -44,6 +48,7 @@ from .attention import verify_attention
 from .acceptance import greedy_tokens, accept_request, argmax_accept, accept_request_rows, argmax_accept_rows
 from .commit import commit_kv
 from .msa import msa_row, tree_path, msa_block_visibility, build_msa_mask
+from .draft import topk_tokens, draft_tree, next_draft
 
 __all__ = [
     "bf16_bits_to_f64", "as_f64",
@@ -53,4 +58,5 @@ __all__ = [
     "greedy_tokens", "accept_request", "argmax_accept", "accept_request_rows", "argmax_accept_rows",
     "commit_kv",
     "msa_row", "tree_path", "msa_block_visibility", "build_msa_mask",
+    "topk_tokens", "draft_tree", "next_draft",
 ]

@@ -59,7 +59,7 @@ def oracle_attention(x, cfg, **kw):
 
 
 def oracle_accept(x, cfg, max_depth):
-    B, T = x["tree_parent"].shape
+    B, T = x["acc_parent"].shape                     # one entry per block row, nodes first
     vrow = np.full((B, T), -1, dtype=np.int32)
     for b in range(B):
         n = int(x["n_nodes"][b])
@@ -216,7 +216,7 @@ def test_msa_full_size_sampled():
                       requests=reqs)
     assert np.isfinite(st.out.cpu().numpy()).all()
     greedy, A, path, last, bonus = oracle_accept(x, cfg, st.max_depth)
-    np.testing.assert_array_equal(st.argmax.cpu().numpy(), greedy)
+    np.testing.assert_array_equal(st.argmax.cpu().numpy()[:, :cfg.T], greedy[:, :cfg.T])
     np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
     np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
     np.testing.assert_array_equal(st.out_bonus.cpu().numpy(), bonus)
