@@ -76,6 +76,7 @@ typedef enum {
 #define SPEC_MAX_NODES 256     /* acceptance nodes per request             */
 #define SPEC_MAX_DEPTH 16      /* longest accepted path                    */
 #define SPEC_MAX_SOFT 256      /* soft-prompt rows                          */
+#define SPEC_MAX_TOPK 8        /* tokens per speculative stream in a draft  */
 
 /* Shape and layout of one verify-attention call (one transformer layer). */
 typedef struct {
@@ -166,6 +167,45 @@ int spec_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag, const in
 int spec_build_msa_mask(const int32_t* tree_parent, const int32_t* n_nodes, int32_t B, int32_t N,
                         int32_t gamma, int32_t Tq, uint32_t* mask_bits, uint32_t* sp_bits, int32_t* n_q,
                         void* stream);
+
+/*
+ * spec_draft_tree -- the next tree draft from the new root's speculative
+ * streams ([SS] tree draft construction and parallel new draft generation).
+ *
+ * The pass that verifies a draft also drafts the next one.  The new root is
+ * the last node of the accepted path (acc_path[b][acc_len[b]-1]); its gamma
+ * speculative streams sit at block rows n + last*gamma + (j-1), j = 1..gamma,
+ * of the multi-stream layout (spec_build_msa_mask), n = n_nodes[b].  From each
+ * stream's logit row the k best tokens are taken (largest logit first, equal
+ * logits in increasing token order; k = 1 is greedy).  Stream j's tokens are
+ * the children of every node of level j-1 and the root carries root_tok[b]
+ * (the correction token, spec_argmax_accept_rows' out_bonus): a complete
+ * k-ary tree of depth gamma with N = 1 + k + ... + k^gamma nodes, flattened
+ * level by level -- the children of node p are k*p+1 .. k*p+k in the rank
+ * order of their tokens, so tree_parent[v] = (v-1)/k.  It feeds the next
+ * spec_build_msa_mask directly.
+ *
+ *   logits      [B, R, V] float32 or bf16 (logits_dtype), the block's rows;
+ *               finite, or NaN, which is never preferred to a number.
+ *   n_nodes     [B] int32   nodes of the verified tree.
+ *   acc_len     [B] int32, acc_path [B, max_depth] int32: the accepted paths
+ *               (spec_argmax_accept_rows' out_len and out_path).
+ *   root_tok    [B] int32   token of the new root.
+ *   out_topk    [B, gamma, k] int32 out: each stream's k tokens (may be NULL
+ *               only when gamma == 0).
+ *   draft_tok   [B, N] int32 out, tree_parent [B, N] int32 out.
+ *   n_out       [B] int32 out: N, or 0 when request b has no new root (no
+ *               accepted node, a path entry outside [0, n_nodes[b]), or
+ *               n_nodes[b] * (1 + gamma) > R); its out_topk, draft_tok and
+ *               tree_parent entries are then all -1.
+ *
+ * Limits: 0 <= gamma, 1 <= k <= 8, N <= 256, k <= V, 1 <= max_depth <= 16,
+ * 1 <= R <= 256.  B == 0 is a no-op.
+ */
+int spec_draft_tree(const void* logits, int32_t logits_dtype, int32_t B, int32_t R, int32_t V,
+                    const int32_t* n_nodes, const int32_t* acc_len, const int32_t* acc_path, int32_t max_depth,
+                    const int32_t* root_tok, int32_t gamma, int32_t k, int32_t* out_topk, int32_t* draft_tok,
+                    int32_t* tree_parent, int32_t* n_out, void* stream);
 
 /*
  * spec_verify_attn_workspace -- bytes of device workspace spec_verify_attn

@@ -29,11 +29,12 @@ SPEC_MAX_TQ = 256
 SPEC_MAX_NODES = 256
 SPEC_MAX_DEPTH = 16
 SPEC_MAX_SOFT = 256
+SPEC_MAX_TOPK = 8
 
 # every symbol the header declares
 EXPORTS = ("spec_build_mask", "spec_build_msa_mask", "spec_verify_attn_workspace", "spec_verify_attn",
-           "spec_argmax_accept",
-           "spec_argmax_accept_rows", "spec_commit_kv", "spec_strerror", "spec_last_error", "spec_version")
+           "spec_argmax_accept", "spec_argmax_accept_rows", "spec_commit_kv", "spec_draft_tree", "spec_strerror",
+           "spec_last_error", "spec_version")
 
 
 class SpecError(RuntimeError):
@@ -69,6 +70,8 @@ def load() -> ctypes.CDLL:
     lib.spec_build_mask.restype = ctypes.c_int
     lib.spec_build_msa_mask.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
     lib.spec_build_msa_mask.restype = ctypes.c_int
+    lib.spec_draft_tree.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _P]
+    lib.spec_draft_tree.restype = ctypes.c_int
     lib.spec_verify_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc)]
     lib.spec_verify_attn_workspace.restype = ctypes.c_size_t
     lib.spec_verify_attn.argtypes = [ctypes.POINTER(AttnDesc)] + [_P] * 14 + [ctypes.c_size_t, _P]
@@ -180,3 +183,12 @@ def spec_last_error() -> str:
 
 def spec_version() -> str:
     return load().spec_version().decode()
+
+
+def spec_draft_tree(logits, logits_dtype, B, R, V, n_nodes, acc_len, acc_path, max_depth, root_tok, gamma, k,
+                    out_topk, draft_tok, tree_parent, n_out, stream=None):
+    lib = load()
+    _check(lib.spec_draft_tree(_ptr(logits), logits_dtype, B, R, V, _ptr(n_nodes), _ptr(acc_len), _ptr(acc_path),
+                               max_depth, _ptr(root_tok), gamma, k, _ptr(out_topk), _ptr(draft_tok),
+                               _ptr(tree_parent), _ptr(n_out), _stream(stream) if B else None),
+           "spec_draft_tree")

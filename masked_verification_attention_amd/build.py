@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 
-SOURCES = ["api.hip", "mask.hip", "attn_valu.hip", "attn_mfma.hip", "accept.hip", "commit.hip"]
+SOURCES = ["api.hip", "mask.hip", "attn_valu.hip", "attn_mfma.hip", "accept.hip", "commit.hip", "draft.hip"]
 ARCH = os.environ.get("SPEC_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU ops are disabled for device code (hipcc's host pass warns

@@ -207,6 +207,41 @@ int spec_build_msa_mask(const int32_t* tree_parent, const int32_t* n_nodes, int3
                     "spec_build_msa_mask launch");
 }
 
+int spec_draft_tree(const void* logits, int32_t logits_dtype, int32_t B, int32_t R, int32_t V,
+                    const int32_t* n_nodes, const int32_t* acc_len, const int32_t* acc_path, int32_t max_depth,
+                    const int32_t* root_tok, int32_t gamma, int32_t k, int32_t* out_topk, int32_t* draft_tok,
+                    int32_t* tree_parent, int32_t* n_out, void* stream) {
+  REQUIRE(B >= 0, SPEC_EINVAL, "B = %d < 0", B);
+  REQUIRE(R >= 1 && R <= SPEC_MAX_TQ, SPEC_EINVAL, "R = %d outside [1, %d]", R, SPEC_MAX_TQ);
+  REQUIRE(k >= 1 && k <= SPEC_MAX_TOPK, SPEC_EINVAL, "k = %d outside [1, %d]", k, SPEC_MAX_TOPK);
+  REQUIRE(gamma >= 0 && gamma < SPEC_MAX_TQ, SPEC_EINVAL, "gamma = %d outside [0, %d)", gamma, SPEC_MAX_TQ);
+  REQUIRE(V >= k, SPEC_EINVAL, "V = %d < k = %d", V, k);
+  REQUIRE(max_depth >= 1 && max_depth <= SPEC_MAX_DEPTH, SPEC_EINVAL, "max_depth = %d outside [1, %d]", max_depth,
+          SPEC_MAX_DEPTH);
+  REQUIRE(logits_dtype == SPEC_F32 || logits_dtype == SPEC_BF16, SPEC_EINVAL, "logits_dtype = %d is not a spec_dtype",
+          logits_dtype);
+  int64_t N = 1, level = 1;
+  for (int g = 1; g <= gamma && N <= SPEC_MAX_TQ; ++g) {
+    level *= k;
+    N += level;
+  }
+  REQUIRE(N <= SPEC_MAX_TQ, SPEC_EINVAL, "a %d-ary tree of depth %d has more than %d nodes", k, gamma, SPEC_MAX_TQ);
+  REQUIRE((int64_t)B * gamma <= 0x7fffffff && (int64_t)B * R <= 0x7fffffff, SPEC_EUNSUPPORTED, "B too large");
+  if (B == 0) return ok();
+  REQUIRE(logits && n_nodes && acc_len && acc_path && root_tok && draft_tok && tree_parent && n_out &&
+              (out_topk || gamma == 0),
+          SPEC_EINVAL, "logits, n_nodes, acc_len, acc_path, root_tok, out_topk, draft_tok, tree_parent and n_out "
+          "must be non-NULL");
+  REQUIRE(aligned(logits, esize_of(logits_dtype)), SPEC_EINVAL, "logits must be aligned to its element size");
+  REQUIRE(aligned(n_nodes, 4) && aligned(acc_len, 4) && aligned(acc_path, 4) && aligned(root_tok, 4) &&
+              aligned(out_topk, 4) && aligned(draft_tok, 4) && aligned(tree_parent, 4) && aligned(n_out, 4),
+          SPEC_EINVAL, "int32 arrays must be 4-byte aligned");
+  return hip_status(sv::launch_draft_tree(logits, logits_dtype, B, R, V, n_nodes, acc_len, acc_path, max_depth,
+                                          root_tok, gamma, k, (int)N, out_topk, draft_tok, tree_parent, n_out,
+                                          static_cast<hipStream_t>(stream)),
+                    "spec_draft_tree launch");
+}
+
 size_t spec_verify_attn_workspace(const spec_attn_desc* d) {
   if (check_desc(d) != SPEC_OK) return 0;
   return sv::plan_attn(*d).ws_bytes;

@@ -1,0 +1,273 @@
+// The next tree draft ("Speculative Streaming", tree draft construction and
+// parallel new draft generation).
+//
+// The pass that verifies a draft also drafts the next one: the gamma
+// speculative streams of the last accepted node -- the new root -- each give a
+// logit row; stream j's k best tokens become the children of every node of
+// level j - 1, under the correction token at the root.  The result is a
+// complete k-ary tree of depth gamma, flattened level by level (the children
+// of node p are k p + 1 .. k p + k, in the rank order of their tokens).
+//
+// k_topk_streams: one workgroup of 1024 threads per (request, stream).  Each
+// thread streams its share of the row with 16-byte loads (eight in flight)
+// and keeps a sorted list of its k best (value, index) pairs; each wave then
+// draws its k best by k rounds of a wave-wide "larger value, then lower
+// index" reduction in which the winning lane pops its list head, and one wave
+// repeats that over the waves' lists.  Ties resolve to the lower token index;
+// -0 equals +0; NaN is never preferred to a number.
+//
+// k_draft_tree: one workgroup per request writes tokens and parents.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace sv {
+
+constexpr int kTopThreads = 1024;
+constexpr int kTopWaves = kTopThreads / kWave;
+
+// (v, i) ranks before (bv, bi): larger value, then lower index
+__device__ __forceinline__ bool ranks_before(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// First stream row of request b's new root in the multi-stream layout, or -1
+// when there is none: no accepted node, a path entry outside the tree, or
+// stream rows past the block.
+__device__ __forceinline__ int root_stream_row(int b, int R, int gamma, const int32_t* n_nodes,
+                                               const int32_t* acc_len, const int32_t* acc_path,
+                                               int max_depth) {
+  const int A = acc_len[b];
+  if (A < 1 || A > max_depth) return -1;
+  const int last = acc_path[(int64_t)b * max_depth + A - 1];
+  const int n = n_nodes[b];
+  if (n < 1 || last < 0 || last >= n || (int64_t)n * (1 + gamma) > R) return -1;
+  return n + last * gamma;
+}
+
+// Sorted list of the K best pairs held by one lane (slots >= k stay empty).
+template <int K>
+struct TopList {
+  float v[K];
+  int i[K];
+  float tail_v;   // the k-th kept pair: anything not ranking before it is dropped
+  int tail_i;
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      v[s] = -INFINITY;
+      i[s] = 0x7fffffff;
+    }
+    tail_v = -INFINITY;
+    tail_i = 0x7fffffff;
+  }
+  // one compare for most values; an insertion is a pass of compare-and-swap
+  // down the list (static indices keep it in registers), the displaced pair
+  // moving on to the next slot
+  __device__ __forceinline__ void push(float x, int xi, int k) {
+    if (!ranks_before(x, xi, tail_v, tail_i)) return;
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      if (s < k && ranks_before(x, xi, v[s], i[s])) {
+        const float tv = v[s];
+        const int ti = i[s];
+        v[s] = x;
+        i[s] = xi;
+        x = tv;
+        xi = ti;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      if (s == k - 1) {
+        tail_v = v[s];
+        tail_i = i[s];
+      }
+    }
+  }
+  __device__ __forceinline__ void pop() {
+#pragma unroll
+    for (int s = 0; s + 1 < K; ++s) {
+      v[s] = v[s + 1];
+      i[s] = i[s + 1];
+    }
+    v[K - 1] = -INFINITY;
+    i[K - 1] = 0x7fffffff;
+  }
+};
+
+// k rounds over a wave: every lane offers its list head, the wave agrees on
+// the best, the owner pops it.  Returns round r's pair in (ov[r], oi[r]) on
+// every lane.
+template <int K>
+__device__ __forceinline__ void wave_topk(TopList<K>& L, int k, float (&ov)[K], int (&oi)[K]) {
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    if (r >= k) break;
+    float bv = L.v[0];
+    int bi = L.i[0];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float xv = __shfl_xor(bv, o);
+      const int xi = __shfl_xor(bi, o);
+      if (ranks_before(xv, xi, bv, bi)) {
+        bv = xv;
+        bi = xi;
+      }
+    }
+    ov[r] = bv;
+    oi[r] = bi;
+    if (L.i[0] == bi && bi != 0x7fffffff) L.pop();
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float logit_at(const T* p, int i);
+template <>
+__device__ __forceinline__ float logit_at<float>(const float* p, int i) { return p[i]; }
+template <>
+__device__ __forceinline__ float logit_at<uint16_t>(const uint16_t* p, int i) {
+  return __uint_as_float(uint32_t(p[i]) << 16);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kTopThreads) void k_topk_streams(
+    const T* __restrict__ logits, int R, int V, const int32_t* __restrict__ n_nodes,
+    const int32_t* __restrict__ acc_len, const int32_t* __restrict__ acc_path, int max_depth, int gamma,
+    int k, int32_t* __restrict__ out_topk) {
+  constexpr int K = SPEC_MAX_TOPK;
+  constexpr int E = 16 / sizeof(T);   // elements per 16-byte load
+  constexpr int U = 8;                // loads in flight per thread
+  __shared__ float wv[kTopWaves][K];
+  __shared__ int wi[kTopWaves][K];
+  const int b = blockIdx.x / gamma;
+  const int j = blockIdx.x % gamma;
+  const int tid = threadIdx.x;
+  int32_t* dst = out_topk + ((int64_t)b * gamma + j) * k;
+  const int row0 = root_stream_row(b, R, gamma, n_nodes, acc_len, acc_path, max_depth);
+  if (row0 < 0) {   // uniform over the workgroup
+    if (tid < k) dst[tid] = -1;
+    return;
+  }
+  const T* base = logits + ((int64_t)b * R + row0 + j) * V;
+  TopList<K> L;
+  L.clear();
+  const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
+  const int pre = min(V, mis == 0 ? 0 : E - mis);
+  for (int i = tid; i < pre; i += kTopThreads) L.push(logit_at<T>(base, i), i, k);
+  const int nvec = (V - pre) / E;
+  const char* vb = reinterpret_cast<const char*>(base + pre);
+  constexpr int RV = U * kTopThreads;   // vectors per round
+  for (int r0 = 0; r0 < nvec; r0 += RV) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = r0 + u * kTopThreads + tid;
+      x[u] = c < nvec ? ldg16_stream(vb + (int64_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = r0 + u * kTopThreads + tid;
+      if (c >= nvec) continue;
+      const int i0 = pre + c * E;
+      const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+      // most values lose to the list's last kept slot: one compare each
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          L.push(bf16lo(w[e]), i0 + 2 * e, k);
+          L.push(bf16hi(w[e]), i0 + 2 * e + 1, k);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) L.push(__uint_as_float(w[e]), i0 + e, k);
+      }
+    }
+  }
+  for (int i = pre + nvec * E + tid; i < V; i += kTopThreads) L.push(logit_at<T>(base, i), i, k);
+
+  float ov[K];
+  int oi[K];
+  wave_topk<K>(L, k, ov, oi);
+  const int wave = tid / kWave, lane = tid % kWave;
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      wv[wave][r] = r < k ? ov[r] : -INFINITY;
+      wi[wave][r] = r < k ? oi[r] : 0x7fffffff;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  L.clear();
+  if (lane < kTopWaves) {
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      L.v[r] = wv[lane][r];
+      L.i[r] = wi[lane][r];
+    }
+  }
+  wave_topk<K>(L, k, ov, oi);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < K; ++r)
+      if (r < k) dst[r] = oi[r] == 0x7fffffff ? -1 : oi[r];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_draft_tree(int R, int gamma, int k, int N,
+                                                    const int32_t* __restrict__ n_nodes,
+                                                    const int32_t* __restrict__ acc_len,
+                                                    const int32_t* __restrict__ acc_path, int max_depth,
+                                                    const int32_t* __restrict__ root_tok,
+                                                    const int32_t* __restrict__ topk,
+                                                    int32_t* __restrict__ draft_tok,
+                                                    int32_t* __restrict__ tree_parent,
+                                                    int32_t* __restrict__ n_out) {
+  const int b = blockIdx.x;
+  const bool ok = root_stream_row(b, R, gamma, n_nodes, acc_len, acc_path, max_depth) >= 0;
+  for (int v = threadIdx.x; v < N; v += blockDim.x) {
+    int tok = -1, par = -1;
+    if (ok) {
+      if (v == 0) {
+        tok = root_tok[b];
+      } else {
+        // level g holds nodes [first, first + k^g); node v is the ((v-1) % k)-th
+        // child of node (v-1) / k
+        int first = 1, cnt = k, g = 1;
+        while (v >= first + cnt) {
+          first += cnt;
+          cnt *= k;
+          ++g;
+        }
+        par = (v - 1) / k;
+        tok = topk[((int64_t)b * gamma + (g - 1)) * k + (v - 1) % k];
+      }
+    }
+    draft_tok[(int64_t)b * N + v] = tok;
+    tree_parent[(int64_t)b * N + v] = par;
+  }
+  if (threadIdx.x == 0) n_out[b] = ok ? N : 0;
+}
+
+hipError_t launch_draft_tree(const void* logits, int dtype, int B, int R, int V, const int32_t* n_nodes,
+                             const int32_t* acc_len, const int32_t* acc_path, int max_depth,
+                             const int32_t* root_tok, int gamma, int k, int N, int32_t* out_topk,
+                             int32_t* draft_tok, int32_t* tree_parent, int32_t* n_out, hipStream_t st) {
+  if (gamma > 0) {
+    const dim3 grid((unsigned)((int64_t)B * gamma));
+    if (dtype == SPEC_BF16)
+      hipLaunchKernelGGL(k_topk_streams<uint16_t>, grid, dim3(kTopThreads), 0, st,
+                         static_cast<const uint16_t*>(logits), R, V, n_nodes, acc_len, acc_path, max_depth, gamma,
+                         k, out_topk);
+    else
+      hipLaunchKernelGGL(k_topk_streams<float>, grid, dim3(kTopThreads), 0, st, static_cast<const float*>(logits),
+                         R, V, n_nodes, acc_len, acc_path, max_depth, gamma, k, out_topk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_draft_tree, dim3(B), dim3(256), 0, st, R, gamma, k, N, n_nodes, acc_len, acc_path,
+                     max_depth, root_tok, out_topk, draft_tok, tree_parent, n_out);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -57,6 +57,10 @@ hipError_t launch_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag,
 hipError_t launch_build_msa_mask(const int32_t* tree_parent, const int32_t* n_nodes, int B, int N,
                                  int gamma, int Tq, uint32_t* mask_bits, uint32_t* sp_bits,
                                  int32_t* n_q, hipStream_t st);
+hipError_t launch_draft_tree(const void* logits, int dtype, int B, int R, int V, const int32_t* n_nodes,
+                             const int32_t* acc_len, const int32_t* acc_path, int max_depth,
+                             const int32_t* root_tok, int gamma, int k, int N, int32_t* out_topk,
+                             int32_t* draft_tok, int32_t* tree_parent, int32_t* n_out, hipStream_t st);
 hipError_t launch_attn_valu(const AttnArgs& a, int dtype, hipStream_t st);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);

@@ -3,7 +3,8 @@
 Uploads one seeded workload (``workloads.generate``) to HBM as torch tensors,
 allocates every output, and runs the four entry points on one stream:
 spec_build_mask -> spec_verify_attn -> spec_argmax_accept -> spec_commit_kv
-(multi-stream workloads: spec_build_msa_mask and spec_argmax_accept_rows).
+(multi-stream workloads: spec_build_msa_mask, spec_argmax_accept_rows and
+spec_draft_tree for the next draft).
 This module only moves memory and marshals arguments; all arithmetic runs in
 the HIP kernels.  torch supplies the device memory and the stream.
 """
@@ -83,7 +84,9 @@ class VerifyStep:
         self.logits = to_device(x["logits"], cfg.logits_dtype, dev) if "logits" in x else None
         self.V = x["logits"].shape[2] if "logits" in x else cfg.V
         # multi-stream rows: the mask comes from the tree, and a node is verified by its
-        # parent's main-stream row (main rows are the first rows of the block)
+        # parent's main-stream row; main rows are the first rows of the block, so the
+        # acceptance parents (the tree, padded with -1 to one entry per row) are also
+        # the verification rows
         self.msa = cfg.structure == "msa_tree"
         self.tree_parent = to_device(x["tree_parent"], "i32", dev) if self.msa else None
 
@@ -96,6 +99,14 @@ class VerifyStep:
         self.out_len = torch.empty(self.B, **i32)
         self.out_path = torch.empty(self.B, self.max_depth, **i32)
         self.out_bonus = torch.empty(self.B, **i32)
+        if self.msa:
+            # the next draft: k tokens per stream of the new root, a complete k-ary tree
+            k, g = cfg.branch, cfg.gamma
+            self.draft_N = sum(k ** e for e in range(g + 1))
+            self.next_topk = torch.empty(self.B, max(g, 1), k, **i32)
+            self.next_tok = torch.empty(self.B, self.draft_N, **i32)
+            self.next_parent = torch.empty(self.B, self.draft_N, **i32)
+            self.next_n = torch.empty(self.B, **i32)
         self.cache_len_out = torch.empty(self.B, **i32)
 
         Hkv, D = cfg.Hkv, cfg.D
@@ -134,7 +145,7 @@ class VerifyStep:
     def argmax_accept(self, stream=None):
         if self.msa:
             bd.spec_argmax_accept_rows(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.T, self.V,
-                                       self.n_nodes, self.draft_tok, self.acc_parent, self.tree_parent,
+                                       self.n_nodes, self.draft_tok, self.acc_parent, self.acc_parent,
                                        self.max_depth, self.argmax, self.out_len, self.out_path,
                                        self.out_bonus, stream)
             return
@@ -147,9 +158,18 @@ class VerifyStep:
                           self.cache_len if in_place else self.cache_len_out, self.k_blk, self.v_blk,
                           self.out_len, self.out_path, self.max_depth, stream)
 
+    def draft(self, stream=None):
+        """The next tree draft from the new root's speculative streams (multi-stream workloads)."""
+        bd.spec_draft_tree(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.Tq, self.V, self.n_nodes,
+                           self.out_len, self.out_path, self.max_depth, self.out_bonus, self.cfg.gamma,
+                           self.cfg.branch, self.next_topk, self.next_tok, self.next_parent, self.next_n, stream)
+
     def run(self, stream=None):
-        """One pass of the whole hot path (the cache length is not advanced in place)."""
+        """One pass of the whole hot path (the cache length is not advanced in place);
+        multi-stream workloads also draft the next tree in the same pass."""
         self.build_mask(stream)
         self.attention(stream)
         self.argmax_accept(stream)
         self.commit(stream)
+        if self.msa:
+            self.draft(stream)

@@ -173,7 +173,18 @@ def test_msa_step_small(case):
     k_host, v_host = st.cache_host()
     np.testing.assert_array_equal(k_host, kc)
     np.testing.assert_array_equal(v_host, vc)
+    check_next_draft(st, x, cfg, A, path, bonus)
     say(f"    accepted lengths {A.tolist()}, bonus {bonus.tolist()}")
+
+
+def check_next_draft(st, x, cfg, A, path, bonus):
+    """The next draft drawn in the same pass from the new root's speculative streams."""
+    r_topk, r_tok, r_par, r_n = oracle.next_draft(x["logits"], cfg.logits_dtype, x["n_nodes"], A, path, bonus,
+                                                  cfg.gamma, cfg.branch)
+    np.testing.assert_array_equal(st.next_topk.cpu().numpy(), r_topk)
+    np.testing.assert_array_equal(st.next_tok.cpu().numpy(), r_tok)
+    np.testing.assert_array_equal(st.next_parent.cpu().numpy(), r_par)
+    np.testing.assert_array_equal(st.next_n.cpu().numpy(), r_n)
 
 
 def test_main_streams_ignore_stream_rows_bitwise():
@@ -226,4 +237,5 @@ def test_msa_full_size_sampled():
     for b in range(cfg.B):
         for d in range(int(A[b])):
             np.testing.assert_array_equal(k_host[b, L[b] + d], x["k_blk"][b, path[b, d]])
+    check_next_draft(st, x, cfg, A, path, bonus)
     say(f"    accepted lengths {A.tolist()}")
