@@ -8,13 +8,16 @@
 // complete k-ary tree of depth gamma, flattened level by level (the children
 // of node p are k p + 1 .. k p + k, in the rank order of their tokens).
 //
-// k_topk_streams: one workgroup of 1024 threads per (request, stream).  Each
-// thread streams its share of the row with 16-byte loads (eight in flight)
-// and keeps a sorted list of its k best (value, index) pairs; each wave then
-// draws its k best by k rounds of a wave-wide "larger value, then lower
-// index" reduction in which the winning lane pops its list head, and one wave
-// repeats that over the waves' lists.  Ties resolve to the lower token index;
-// -0 equals +0; NaN is never preferred to a number.
+// k_topk_streams: one workgroup of 1024 threads per (request, stream), two
+// passes over the row with 16-byte loads (eight in flight per thread).  Pass
+// 1 takes each thread's largest value; the k-th largest of those values is a
+// lower bound on the row's k-th best, since it is met by k distinct elements.
+// Pass 2 (the row is then resident in L2) keeps, per thread, a sorted list of
+// the few candidates at or above the bound.  The lists are merged by k rounds
+// of a wave-wide "larger value, then lower index" reduction in which the
+// winning lane pops its list head, first within each wave, then over the
+// waves.  Ties resolve to the lower token index; -0 equals +0; NaN is never
+// preferred to a number.
 //
 // k_draft_tree: one workgroup per request writes tokens and parents.
 #include "device_common.hpp"
@@ -49,22 +52,16 @@ template <int K>
 struct TopList {
   float v[K];
   int i[K];
-  float tail_v;   // the k-th kept pair: anything not ranking before it is dropped
-  int tail_i;
   __device__ __forceinline__ void clear() {
 #pragma unroll
     for (int s = 0; s < K; ++s) {
       v[s] = -INFINITY;
       i[s] = 0x7fffffff;
     }
-    tail_v = -INFINITY;
-    tail_i = 0x7fffffff;
   }
-  // one compare for most values; an insertion is a pass of compare-and-swap
-  // down the list (static indices keep it in registers), the displaced pair
-  // moving on to the next slot
+  // insertion by a pass of compare-and-swap down the list (static indices keep
+  // it in registers); the displaced pair moves on, off the end past slot k-1
   __device__ __forceinline__ void push(float x, int xi, int k) {
-    if (!ranks_before(x, xi, tail_v, tail_i)) return;
 #pragma unroll
     for (int s = 0; s < K; ++s) {
       if (s < k && ranks_before(x, xi, v[s], i[s])) {
@@ -74,13 +71,6 @@ struct TopList {
         i[s] = xi;
         x = tv;
         xi = ti;
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < K; ++s) {
-      if (s == k - 1) {
-        tail_v = v[s];
-        tail_i = i[s];
       }
     }
   }
@@ -129,16 +119,84 @@ __device__ __forceinline__ float logit_at<uint16_t>(const uint16_t* p, int i) {
   return __uint_as_float(uint32_t(p[i]) << 16);
 }
 
+// Visit every (value, index) of a row: scalar head up to 16-byte alignment,
+// vector body (U loads in flight per thread), scalar tail.  Each thread sees
+// its own elements in any order.
+template <typename T, int U, typename F>
+__device__ __forceinline__ void for_row(const T* base, int V, int tid, F&& f) {
+  constexpr int E = 16 / sizeof(T);
+  const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
+  const int pre = min(V, mis == 0 ? 0 : E - mis);
+  for (int i = tid; i < pre; i += kTopThreads) f(logit_at<T>(base, i), i);
+  const int nvec = (V - pre) / E;
+  const char* vb = reinterpret_cast<const char*>(base + pre);
+  constexpr int RV = U * kTopThreads;
+  for (int r0 = 0; r0 < nvec; r0 += RV) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = r0 + u * kTopThreads + tid;
+      x[u] = c < nvec ? ldg16(vb + (int64_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = r0 + u * kTopThreads + tid;
+      if (c >= nvec) continue;
+      const int i0 = pre + c * E;
+      const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f(bf16lo(w[e]), i0 + 2 * e);
+          f(bf16hi(w[e]), i0 + 2 * e + 1);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f(__uint_as_float(w[e]), i0 + e);
+      }
+    }
+  }
+  for (int i = pre + nvec * E + tid; i < V; i += kTopThreads) f(logit_at<T>(base, i), i);
+}
+
+// The workgroup's k best pairs of the lanes' sorted lists, valid in wave 0
+// (every lane); uses the LDS staging arrays.
+template <int K>
+__device__ __forceinline__ void block_topk(TopList<K>& L, int k, float (&ov)[K], int (&oi)[K],
+                                           float (&wv)[kTopWaves][K], int (&wi)[kTopWaves][K]) {
+  wave_topk<K>(L, k, ov, oi);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+      wv[wave][r] = r < k ? ov[r] : -INFINITY;
+      wi[wave][r] = r < k ? oi[r] : 0x7fffffff;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    L.clear();
+    if (lane < kTopWaves) {
+#pragma unroll
+      for (int r = 0; r < K; ++r) {
+        L.v[r] = wv[lane][r];
+        L.i[r] = wi[lane][r];
+      }
+    }
+    wave_topk<K>(L, k, ov, oi);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
     const T* __restrict__ logits, int R, int V, const int32_t* __restrict__ n_nodes,
     const int32_t* __restrict__ acc_len, const int32_t* __restrict__ acc_path, int max_depth, int gamma,
     int k, int32_t* __restrict__ out_topk) {
   constexpr int K = SPEC_MAX_TOPK;
-  constexpr int E = 16 / sizeof(T);   // elements per 16-byte load
-  constexpr int U = 8;                // loads in flight per thread
+  constexpr int U = 8;   // loads in flight per thread
   __shared__ float wv[kTopWaves][K];
   __shared__ int wi[kTopWaves][K];
+  __shared__ float bound_v;
   const int b = blockIdx.x / gamma;
   const int j = blockIdx.x % gamma;
   const int tid = threadIdx.x;
@@ -149,65 +207,29 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
     return;
   }
   const T* base = logits + ((int64_t)b * R + row0 + j) * V;
-  TopList<K> L;
-  L.clear();
-  const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
-  const int pre = min(V, mis == 0 ? 0 : E - mis);
-  for (int i = tid; i < pre; i += kTopThreads) L.push(logit_at<T>(base, i), i, k);
-  const int nvec = (V - pre) / E;
-  const char* vb = reinterpret_cast<const char*>(base + pre);
-  constexpr int RV = U * kTopThreads;   // vectors per round
-  for (int r0 = 0; r0 < nvec; r0 += RV) {
-    u32x4 x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = r0 + u * kTopThreads + tid;
-      x[u] = c < nvec ? ldg16_stream(vb + (int64_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = r0 + u * kTopThreads + tid;
-      if (c >= nvec) continue;
-      const int i0 = pre + c * E;
-      const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-      // most values lose to the list's last kept slot: one compare each
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          L.push(bf16lo(w[e]), i0 + 2 * e, k);
-          L.push(bf16hi(w[e]), i0 + 2 * e + 1, k);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) L.push(__uint_as_float(w[e]), i0 + e, k);
-      }
-    }
-  }
-  for (int i = pre + nvec * E + tid; i < V; i += kTopThreads) L.push(logit_at<T>(base, i), i, k);
-
   float ov[K];
   int oi[K];
-  wave_topk<K>(L, k, ov, oi);
-  const int wave = tid / kWave, lane = tid % kWave;
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < K; ++r) {
-      wv[wave][r] = r < k ? ov[r] : -INFINITY;
-      wi[wave][r] = r < k ? oi[r] : 0x7fffffff;
-    }
-  }
-  __syncthreads();
-  if (wave != 0) return;
+
+  // pass 1: each thread's largest value (NaN ignored); the k-th largest of
+  // those values bounds the answer from below
+  float mv = -INFINITY;
+  for_row<T, U>(base, V, tid, [&](float x, int) { mv = fmaxf(mv, x); });
+  TopList<K> L;
   L.clear();
-  if (lane < kTopWaves) {
-#pragma unroll
-    for (int r = 0; r < K; ++r) {
-      L.v[r] = wv[lane][r];
-      L.i[r] = wi[lane][r];
-    }
-  }
-  wave_topk<K>(L, k, ov, oi);
-  if (lane == 0) {
+  L.v[0] = mv;
+  L.i[0] = tid;   // any distinct tag: only the values matter here
+  block_topk<K>(L, k, ov, oi, wv, wi);
+  if (tid == 0) bound_v = ov[k - 1];
+  __syncthreads();
+  const float tv = bound_v;
+
+  // pass 2: sorted lists of the candidates (values >= the bound) only
+  L.clear();
+  for_row<T, U>(base, V, tid, [&](float x, int xi) {
+    if (x >= tv) L.push(x, xi, k);
+  });
+  block_topk<K>(L, k, ov, oi, wv, wi);
+  if (tid == 0) {
 #pragma unroll
     for (int r = 0; r < K; ++r)
       if (r < k) dst[r] = oi[r] == 0x7fffffff ? -1 : oi[r];
