@@ -28,6 +28,9 @@ the slow, obvious way (explicit dense masks, per-request loops, fp64):
 * ``msa``        -- the multi-stream rows of a tree draft and what each sees
                     (Speculative Streaming, Equations 1, 2 and 4, and its
                     batching with speculative streams).
+* ``prob_accept`` -- acceptance by the target's probability of each draft:
+                    Lookahead Attention's threshold rule and Speculative
+                    Streaming's soft matching with given uniforms.
 * ``draft``      -- the next tree draft: per-stream top-k tokens of the last
                     accepted node's streams, linked stream to stream under the
                     correction token (Speculative Streaming, tree draft
@@ -49,6 +52,8 @@ from .acceptance import greedy_tokens, accept_request, argmax_accept, accept_req
 from .commit import commit_kv
 from .msa import msa_row, tree_path, msa_block_visibility, build_msa_mask
 from .draft import topk_tokens, draft_tree, next_draft
+from .prob_accept import (MODE_THRESHOLD, MODE_SOFT, target_prob, node_probs, decide, scan_accepted,
+                          prob_accept)
 
 __all__ = [
     "bf16_bits_to_f64", "as_f64",
@@ -59,4 +64,5 @@ __all__ = [
     "commit_kv",
     "msa_row", "tree_path", "msa_block_visibility", "build_msa_mask",
     "topk_tokens", "draft_tree", "next_draft",
+    "MODE_THRESHOLD", "MODE_SOFT", "target_prob", "node_probs", "decide", "scan_accepted", "prob_accept",
 ]
