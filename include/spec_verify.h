@@ -78,6 +78,10 @@ typedef enum {
 #define SPEC_MAX_SOFT 256      /* soft-prompt rows                          */
 #define SPEC_MAX_TOPK 8        /* tokens per speculative stream in a draft  */
 
+/* acceptance rules of spec_prob_accept */
+#define SPEC_ACCEPT_THRESHOLD 1 /* [LA]: target probability of the draft > threshold          */
+#define SPEC_ACCEPT_SOFT 2      /* [SS] soft matching: accept with probability min(1, p/p_d) */
+
 /* Shape and layout of one verify-attention call (one transformer layer). */
 typedef struct {
   int32_t B;       /* requests                                                */
@@ -167,6 +171,42 @@ int spec_build_mask(const int32_t* attn_parent, const uint8_t* sp_flag, const in
 int spec_build_msa_mask(const int32_t* tree_parent, const int32_t* n_nodes, int32_t B, int32_t N,
                         int32_t gamma, int32_t Tq, uint32_t* mask_bits, uint32_t* sp_bits, int32_t* n_q,
                         void* stream);
+
+/*
+ * spec_prob_accept -- acceptance by the target's probability of each draft.
+ *
+ * The scan of spec_argmax_accept_rows (a node counts only if its whole root
+ * path is accepted; longest path, depth-first-first among equals; an explicit
+ * root, verification row -1, is accepted unchecked; a row outside [0, n)
+ * never accepts; the correction token is the greedy token of the last
+ * accepted node's row), with the per-node decision taken on
+ * p = softmax(logits[b, u])[draft_tok[b, v]], u the node's verification row:
+ *   SPEC_ACCEPT_THRESHOLD  p > threshold ([LA] verification: each proposal's
+ *                          probability exceeds a threshold; longest prefix);
+ *   SPEC_ACCEPT_SOFT       uniform[b,v] * draft_prob[b,v] < p, i.e. acceptance
+ *                          with probability min(1, p / p_draft) for a uniform
+ *                          draw in [0, 1) ([SS] verification, soft matching
+ *                          after Leviathan et al.; the draw is an input).
+ * p is computed in float32 from the row's log-sum-exp (one streaming pass per
+ * row that also yields the greedy token).
+ *
+ *   logits, logits_dtype, B, T, V, n_nodes, draft_tok, acc_parent,
+ *   verify_row (NULL = row v verifies node v), max_depth, out_argmax,
+ *   out_len, out_path, out_bonus (may be NULL): as spec_argmax_accept_rows.
+ *   threshold   SPEC_ACCEPT_THRESHOLD: finite, >= 0.
+ *   draft_prob  [B, T] float: SPEC_ACCEPT_SOFT only, the draft's probability
+ *               of its token (0 = accept iff p > 0).
+ *   uniform     [B, T] float: SPEC_ACCEPT_SOFT only, draws in [0, 1).
+ *   out_prob    [B, T] float out: p of each node (1 for the unchecked root, 0
+ *               for a row or token out of range; NaN past n_nodes[b]).
+ *
+ * Limits as spec_argmax_accept_rows; logits must be finite.
+ */
+int spec_prob_accept(const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,
+                     const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
+                     const int32_t* verify_row, int32_t max_depth, int32_t mode, float threshold,
+                     const float* draft_prob, const float* uniform, int32_t* out_argmax, float* out_prob,
+                     int32_t* out_len, int32_t* out_path, int32_t* out_bonus, void* stream);
 
 /*
  * spec_draft_tree -- the next tree draft from the new root's speculative

@@ -30,11 +30,13 @@ SPEC_MAX_NODES = 256
 SPEC_MAX_DEPTH = 16
 SPEC_MAX_SOFT = 256
 SPEC_MAX_TOPK = 8
+SPEC_ACCEPT_THRESHOLD = 1
+SPEC_ACCEPT_SOFT = 2
 
 # every symbol the header declares
 EXPORTS = ("spec_build_mask", "spec_build_msa_mask", "spec_verify_attn_workspace", "spec_verify_attn",
-           "spec_argmax_accept", "spec_argmax_accept_rows", "spec_commit_kv", "spec_draft_tree", "spec_strerror",
-           "spec_last_error", "spec_version")
+           "spec_argmax_accept", "spec_argmax_accept_rows", "spec_prob_accept", "spec_commit_kv", "spec_draft_tree",
+           "spec_strerror", "spec_last_error", "spec_version")
 
 
 class SpecError(RuntimeError):
@@ -72,6 +74,9 @@ def load() -> ctypes.CDLL:
     lib.spec_build_msa_mask.restype = ctypes.c_int
     lib.spec_draft_tree.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _P]
     lib.spec_draft_tree.restype = ctypes.c_int
+    lib.spec_prob_accept.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _P,
+                                     _P, _P, _P, _P]
+    lib.spec_prob_accept.restype = ctypes.c_int
     lib.spec_verify_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc)]
     lib.spec_verify_attn_workspace.restype = ctypes.c_size_t
     lib.spec_verify_attn.argtypes = [ctypes.POINTER(AttnDesc)] + [_P] * 14 + [ctypes.c_size_t, _P]
@@ -192,3 +197,14 @@ def spec_draft_tree(logits, logits_dtype, B, R, V, n_nodes, acc_len, acc_path, m
                                max_depth, _ptr(root_tok), gamma, k, _ptr(out_topk), _ptr(draft_tok),
                                _ptr(tree_parent), _ptr(n_out), _stream(stream) if B else None),
            "spec_draft_tree")
+
+
+def spec_prob_accept(logits, logits_dtype, B, T, V, n_nodes, draft_tok, acc_parent, verify_row, max_depth, mode,
+                     threshold, draft_prob, uniform, out_argmax, out_prob, out_len, out_path, out_bonus,
+                     stream=None):
+    lib = load()
+    _check(lib.spec_prob_accept(_ptr(logits), logits_dtype, B, T, V, _ptr(n_nodes), _ptr(draft_tok),
+                                _ptr(acc_parent), _ptr(verify_row), max_depth, mode, float(threshold),
+                                _ptr(draft_prob), _ptr(uniform), _ptr(out_argmax), _ptr(out_prob), _ptr(out_len),
+                                _ptr(out_path), _ptr(out_bonus), _stream(stream) if B else None),
+           "spec_prob_accept")

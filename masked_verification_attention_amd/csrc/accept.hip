@@ -25,6 +25,14 @@
 // correction token is the greedy token of the path's last node's row
 // ("Speculative Streaming", the verification step: one token from the
 // target's logits where the walk stopped).
+//
+// Acceptance by probability (the same scan, other per-node decisions): the
+// target's probability p of a node's draft at its verification row, from
+// the row's log-sum-exp (k_argmax_lse), either exceeds a threshold
+// ("Lookahead Attention", its verification) or beats a given uniform draw
+// scaled by the draft's own probability -- u * p_draft < p, i.e. acceptance
+// with probability min(1, p / p_draft) ("Speculative Streaming", soft
+// matching after Leviathan et al.).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -150,6 +158,131 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ lo
   }
 }
 
+// k_argmax_lse: the greedy token and the log-sum-exp of every node row, for
+// acceptance by probability.  Same stream as k_argmax; each thread also keeps
+// a running maximum m and sum s of exp(x - m) (in the log2 domain), moving m
+// once per 16-byte vector; the workgroup merges (m, s) pairs.  Rows past
+// n_nodes get argmax -1 and a NaN log-sum-exp.
+template <typename T>
+__global__ __launch_bounds__(kArgThreads) void k_argmax_lse(const T* __restrict__ logits, int T_, int V,
+                                                            const int32_t* __restrict__ n_nodes,
+                                                            int32_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int E = 16 / sizeof(T);
+  constexpr int U = 8;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ float sv_[kArgThreads / kWave];
+  __shared__ int si_[kArgThreads / kWave];
+  __shared__ float sm_[kArgThreads / kWave];
+  __shared__ float ss_[kArgThreads / kWave];
+  const int row = blockIdx.x;
+  const int b = row / T_;
+  const int v = row % T_;
+  const int n = clampi(n_nodes[b], 0, T_);
+  if (v >= n) {
+    if (threadIdx.x == 0) {
+      out[row] = -1;
+      lse[row] = __builtin_nanf("");
+    }
+    return;
+  }
+  const T* base = logits + (int64_t)row * V;
+  float bv = -INFINITY, m = -INFINITY, s = 0.f;   // m, s in log2 units
+  int bi = 0x7fffffff;
+  auto add = [&](float x, int i) {
+    better(bv, bi, x, i);
+    const float y = x * kLog2e;
+    if (y > m) {
+      s = m == -INFINITY ? 0.f : s * fast_exp2(m - y);
+      m = y;
+    }
+    if (m != -INFINITY) s += fast_exp2(y - m);
+  };
+  const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
+  const int pre = min(V, mis == 0 ? 0 : E - mis);
+  for (int i = threadIdx.x; i < pre; i += kArgThreads) add(elem_at<T>(base, i), i);
+  const int nvec = (V - pre) / E;
+  const char* vb = reinterpret_cast<const char*>(base + pre);
+  constexpr int RV = U * kArgThreads;
+  for (int r0 = 0; r0 < nvec; r0 += RV) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = r0 + u * kArgThreads + (int)threadIdx.x;
+      x[u] = c < nvec ? ldg16_stream(vb + (int64_t)c * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = r0 + u * kArgThreads + (int)threadIdx.x;
+      if (c >= nvec) continue;
+      const int i0 = pre + c * E;
+      float xs[E];
+      const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xs[2 * e] = bf16lo(w[e]);
+          xs[2 * e + 1] = bf16hi(w[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[e] = __uint_as_float(w[e]);
+      }
+      // indices increase within the vector: a strict ">" keeps the first maximum
+      float cm = xs[0];
+      int ci = i0;
+#pragma unroll
+      for (int e = 1; e < E; ++e)
+        if (xs[e] > cm) {
+          cm = xs[e];
+          ci = i0 + e;
+        }
+      better(bv, bi, cm, ci);
+      const float ym = cm * kLog2e;
+      if (ym > m) {
+        s = m == -INFINITY ? 0.f : s * fast_exp2(m - ym);
+        m = ym;
+      }
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s += fast_exp2(xs[e] * kLog2e - m);
+      }
+    }
+  }
+  for (int i = pre + nvec * E + threadIdx.x; i < V; i += kArgThreads) add(elem_at<T>(base, i), i);
+
+  auto merge = [&](float om, float os) {
+    const float M = fmaxf(m, om);
+    if (M == -INFINITY) return;
+    s = (m == -INFINITY ? 0.f : s * fast_exp2(m - M)) + (om == -INFINITY ? 0.f : os * fast_exp2(om - M));
+    m = M;
+  };
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    better(bv, bi, ov, oi);
+    const float om = __shfl_xor(m, o);
+    const float os = __shfl_xor(s, o);
+    merge(om, os);
+  }
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) {
+    sv_[wave] = bv;
+    si_[wave] = bi;
+    sm_[wave] = m;
+    ss_[wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kArgThreads / kWave; ++w) {
+      better(bv, bi, sv_[w], si_[w]);
+      merge(sm_[w], ss_[w]);
+    }
+    out[row] = bi == 0x7fffffff ? 0 : bi;
+    lse[row] = (m + fast_log2(s)) * 0.69314718055994531f;
+  }
+}
+
 constexpr int kAccThreads = 256;   // >= SPEC_MAX_NODES: one thread per node
 
 __device__ __forceinline__ bool key_less(uint64_t ah, uint64_t al, uint64_t bh, uint64_t bl) {
@@ -163,9 +296,10 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
                                                         const int32_t* __restrict__ argmax, int max_depth,
                                                         int32_t* __restrict__ out_len,
                                                         int32_t* __restrict__ out_path,
-                                                        int32_t* __restrict__ out_bonus) {
+                                                        int32_t* __restrict__ out_bonus, AcceptRule rule) {
   __shared__ int32_t par[SPEC_MAX_NODES];
   __shared__ uint8_t okv[SPEC_MAX_NODES];
+  __shared__ float row_lse[SPEC_MAX_NODES];
   __shared__ int red_i[kAccThreads / kWave];
   __shared__ uint64_t red_h[kAccThreads / kWave];
   __shared__ uint64_t red_l[kAccThreads / kWave];
@@ -175,13 +309,36 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
   const int n = clampi(n_nodes[b], 0, T_);
   const int wave = v / kWave;
   const int lane = v % kWave;
+  // probability rules: every row's log-sum-exp is staged before the same
+  // buffer receives the nodes' probabilities
+  if (rule.mode != 0 && v < n) row_lse[v] = rule.prob[(int64_t)b * T_ + v];
+  __syncthreads();
   if (v < n) {
     par[v] = acc_parent[(int64_t)b * T_ + v];
-    // the row whose greedy token verifies node v: v itself, or the given row
-    // (-1 = accepted unchecked; a row outside [0, n) never matches)
+    // the row that verifies node v: v itself, or the given row (-1 = accepted
+    // unchecked; a row outside [0, n) never accepts)
     const int u = verify_row ? verify_row[(int64_t)b * T_ + v] : v;
-    okv[v] = u == -1 ? 1
-                     : ((u >= 0 && u < n && draft_tok[(int64_t)b * T_ + v] == argmax[(int64_t)b * T_ + u]) ? 1 : 0);
+    const int x = draft_tok[(int64_t)b * T_ + v];
+    const bool in_rows = u >= 0 && u < n;
+    if (rule.mode == 0) {
+      okv[v] = u == -1 ? 1 : ((in_rows && x == argmax[(int64_t)b * T_ + u]) ? 1 : 0);
+    } else {
+      // target probability of the draft at its row: exp(logit - lse)
+      float p = u == -1 ? 1.f : 0.f;
+      if (in_rows && x >= 0 && x < rule.V) {
+        const int64_t at = ((int64_t)b * T_ + u) * rule.V + x;
+        const float l = rule.logits_bf16 ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(rule.logits)[at]) << 16)
+                                         : static_cast<const float*>(rule.logits)[at];
+        p = fast_exp2((l - row_lse[u]) * 1.4426950408889634f);
+      }
+      bool ok;
+      if (u == -1) ok = true;
+      else if (!in_rows) ok = false;
+      else if (rule.mode == 1) ok = p > rule.threshold;
+      else ok = rule.uniform[(int64_t)b * T_ + v] * rule.draft_prob[(int64_t)b * T_ + v] < p;
+      okv[v] = ok ? 1 : 0;
+      rule.prob[(int64_t)b * T_ + v] = p;
+    }
   }
   __syncthreads();
 
@@ -290,12 +447,24 @@ hipError_t launch_argmax(const void* logits, int dtype, int B, int T, int V, con
   return hipGetLastError();
 }
 
+hipError_t launch_argmax_lse(const void* logits, int dtype, int B, int T, int V, const int32_t* n_nodes,
+                             int32_t* out_argmax, float* out_lse, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)B * T));
+  if (dtype == SPEC_F32)
+    hipLaunchKernelGGL(k_argmax_lse<float>, grid, dim3(kArgThreads), 0, st, static_cast<const float*>(logits), T,
+                       V, n_nodes, out_argmax, out_lse);
+  else
+    hipLaunchKernelGGL(k_argmax_lse<uint16_t>, grid, dim3(kArgThreads), 0, st,
+                       static_cast<const uint16_t*>(logits), T, V, n_nodes, out_argmax, out_lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_accept(int B, int T, const int32_t* n_nodes, const int32_t* draft_tok,
                          const int32_t* acc_parent, const int32_t* verify_row, const int32_t* argmax,
                          int max_depth, int32_t* out_len, int32_t* out_path, int32_t* out_bonus,
-                         hipStream_t st) {
+                         const AcceptRule& rule, hipStream_t st) {
   hipLaunchKernelGGL(k_accept, dim3(B), dim3(kAccThreads), 0, st, T, n_nodes, draft_tok, acc_parent, verify_row,
-                     argmax, max_depth, out_len, out_path, out_bonus);
+                     argmax, max_depth, out_len, out_path, out_bonus, rule);
   return hipGetLastError();
 }
 

@@ -149,8 +149,9 @@ int argmax_accept_impl(const char* fn, const void* logits, int32_t logits_dtype,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = sv::launch_argmax(logits, logits_dtype, B, T, V, n_nodes, out_argmax, s);
   if (e != hipSuccess) return hip_status(e, "argmax launch");
+  sv::AcceptRule greedy{};
   e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, verify_row, out_argmax, max_depth, out_len,
-                        out_path, out_bonus, s);
+                        out_path, out_bonus, greedy, s);
   return hip_status(e, "acceptance scan launch");
 }
 
@@ -240,6 +241,51 @@ int spec_draft_tree(const void* logits, int32_t logits_dtype, int32_t B, int32_t
                                           root_tok, gamma, k, (int)N, out_topk, draft_tok, tree_parent, n_out,
                                           static_cast<hipStream_t>(stream)),
                     "spec_draft_tree launch");
+}
+
+int spec_prob_accept(const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,
+                     const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
+                     const int32_t* verify_row, int32_t max_depth, int32_t mode, float threshold,
+                     const float* draft_prob, const float* uniform, int32_t* out_argmax, float* out_prob,
+                     int32_t* out_len, int32_t* out_path, int32_t* out_bonus, void* stream) {
+  REQUIRE(B >= 0, SPEC_EINVAL, "B = %d < 0", B);
+  REQUIRE(T >= 1 && T <= SPEC_MAX_NODES, SPEC_EINVAL, "T = %d outside [1, %d]", T, SPEC_MAX_NODES);
+  REQUIRE(V >= 1, SPEC_EINVAL, "V = %d < 1", V);
+  REQUIRE(max_depth >= 1 && max_depth <= SPEC_MAX_DEPTH, SPEC_EINVAL, "max_depth = %d outside [1, %d]", max_depth,
+          SPEC_MAX_DEPTH);
+  REQUIRE(logits_dtype == SPEC_F32 || logits_dtype == SPEC_BF16, SPEC_EINVAL, "logits_dtype = %d is not a spec_dtype",
+          logits_dtype);
+  REQUIRE(mode == SPEC_ACCEPT_THRESHOLD || mode == SPEC_ACCEPT_SOFT, SPEC_EINVAL,
+          "mode = %d (SPEC_ACCEPT_THRESHOLD or SPEC_ACCEPT_SOFT)", mode);
+  REQUIRE(mode != SPEC_ACCEPT_THRESHOLD || (isfinite(threshold) && threshold >= 0.f), SPEC_EINVAL,
+          "threshold must be finite and >= 0");
+  REQUIRE((int64_t)B * T <= 0x7fffffff && (int64_t)B * T * V < (int64_t(1) << 46), SPEC_EUNSUPPORTED,
+          "B * T * V too large");
+  if (B == 0) return ok();
+  REQUIRE(logits && n_nodes && draft_tok && acc_parent && out_argmax && out_prob && out_len && out_path, SPEC_EINVAL,
+          "logits, n_nodes, draft_tok, acc_parent and the outputs argmax, prob, len, path must be non-NULL");
+  REQUIRE(mode != SPEC_ACCEPT_SOFT || (draft_prob && uniform), SPEC_EINVAL,
+          "soft matching needs draft_prob and uniform");
+  REQUIRE(aligned(logits, esize_of(logits_dtype)), SPEC_EINVAL, "logits must be aligned to its element size");
+  REQUIRE(aligned(n_nodes, 4) && aligned(draft_tok, 4) && aligned(acc_parent, 4) && aligned(verify_row, 4) &&
+              aligned(draft_prob, 4) && aligned(uniform, 4) && aligned(out_argmax, 4) && aligned(out_prob, 4) &&
+              aligned(out_len, 4) && aligned(out_path, 4) && aligned(out_bonus, 4),
+          SPEC_EINVAL, "int32 / float arrays must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = sv::launch_argmax_lse(logits, logits_dtype, B, T, V, n_nodes, out_argmax, out_prob, s);
+  if (e != hipSuccess) return hip_status(e, "argmax / log-sum-exp launch");
+  sv::AcceptRule rule{};
+  rule.mode = mode;
+  rule.threshold = threshold;
+  rule.draft_prob = draft_prob;
+  rule.uniform = uniform;
+  rule.logits = logits;
+  rule.logits_bf16 = logits_dtype == SPEC_BF16;
+  rule.V = V;
+  rule.prob = out_prob;
+  e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, verify_row, out_argmax, max_depth, out_len, out_path,
+                        out_bonus, rule, s);
+  return hip_status(e, "acceptance scan launch");
 }
 
 size_t spec_verify_attn_workspace(const spec_attn_desc* d) {

@@ -66,11 +66,25 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);
 hipError_t launch_argmax(const void* logits, int dtype, int B, int T, int V, const int32_t* n_nodes,
                          int32_t* out_argmax, hipStream_t st);
+// Per-node acceptance decision of k_accept.
+struct AcceptRule {
+  int mode;                 // 0: the draft equals the row's greedy token; 1: p > threshold; 2: u * p_draft < p
+  float threshold;          // mode 1
+  const float* draft_prob;  // mode 2: [B, T]
+  const float* uniform;     // mode 2: [B, T]
+  const void* logits;       // modes 1, 2: [B, T, V], for the draft's logit
+  int logits_bf16;
+  int V;
+  float* prob;              // modes 1, 2: [B, T]; in: each row's log-sum-exp, out: each node's p
+};
+
+hipError_t launch_argmax_lse(const void* logits, int dtype, int B, int T, int V, const int32_t* n_nodes,
+                             int32_t* out_argmax, float* out_lse, hipStream_t st);
 // verify_row == nullptr: row v verifies node v; out_bonus may be nullptr
 hipError_t launch_accept(int B, int T, const int32_t* n_nodes, const int32_t* draft_tok,
                          const int32_t* acc_parent, const int32_t* verify_row, const int32_t* argmax,
                          int max_depth, int32_t* out_len, int32_t* out_path, int32_t* out_bonus,
-                         hipStream_t st);
+                         const AcceptRule& rule, hipStream_t st);
 hipError_t launch_commit(int B, int Tq, int Hkv, int D, int esize, int64_t lmax, int64_t sb,
                          int64_t sl, int64_t sh, void* k_cache, void* v_cache,
                          const int32_t* cache_len_in, int32_t* cache_len_out, const void* k_blk,

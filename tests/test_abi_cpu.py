@@ -108,6 +108,8 @@ def test_empty_batch_is_a_noop_without_touching_memory():
     attn(good_desc(B=0), q=None, out=None)
     bd.spec_build_mask(None, None, None, 0, 8, None, None, stream=0)
     bd.spec_build_msa_mask(None, None, 0, 40, 3, 160, None, None, None, stream=0)
+    bd.spec_prob_accept(None, bd.SPEC_BF16, 0, 4, 100, None, None, None, None, 4, bd.SPEC_ACCEPT_SOFT, 0.0, None,
+                        None, None, None, None, None, None, stream=0)
     bd.spec_draft_tree(None, bd.SPEC_BF16, 0, 160, 100, None, None, None, 4, None, 3, 3, None, None, None, None,
                        stream=0)
     bd.spec_argmax_accept(None, bd.SPEC_BF16, 0, 4, 100, None, None, None, 4, None, None, None, stream=0)
@@ -126,6 +128,22 @@ def test_other_entry_points_reject_bad_arguments():
         lambda: bd.spec_build_msa_mask(FAKE, FAKE, 2, 40, 3, 160, FAKE, FAKE, None, stream=0),
         lambda: bd.spec_build_msa_mask(FAKE, FAKE + 1, 2, 40, 3, 160, FAKE, FAKE, FAKE, stream=0),
         lambda: bd.spec_build_msa_mask(FAKE, FAKE, -1, 40, 3, 160, FAKE, FAKE, FAKE, stream=0),
+        # spec_prob_accept: bad mode, negative / NaN threshold, soft without draws, NULL prob, T, misaligned
+        lambda: bd.spec_prob_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, None, 4, 0, 0.5, FAKE, FAKE,
+                                    FAKE, FAKE, FAKE, FAKE, None, stream=0),
+        lambda: bd.spec_prob_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, None, 4,
+                                    bd.SPEC_ACCEPT_THRESHOLD, -0.1, None, None, FAKE, FAKE, FAKE, FAKE, None, stream=0),
+        lambda: bd.spec_prob_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, None, 4,
+                                    bd.SPEC_ACCEPT_THRESHOLD, float("nan"), None, None, FAKE, FAKE, FAKE, FAKE, None,
+                                    stream=0),
+        lambda: bd.spec_prob_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, None, 4, bd.SPEC_ACCEPT_SOFT,
+                                    0.0, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, stream=0),
+        lambda: bd.spec_prob_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, None, 4,
+                                    bd.SPEC_ACCEPT_THRESHOLD, 0.5, None, None, FAKE, None, FAKE, FAKE, None, stream=0),
+        lambda: bd.spec_prob_accept(FAKE, bd.SPEC_BF16, 2, 0, 100, FAKE, FAKE, FAKE, None, 4,
+                                    bd.SPEC_ACCEPT_THRESHOLD, 0.5, None, None, FAKE, FAKE, FAKE, FAKE, None, stream=0),
+        lambda: bd.spec_prob_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, None, 4, bd.SPEC_ACCEPT_SOFT,
+                                    0.0, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, stream=0),
         # spec_draft_tree: k out of range, tree over 256 nodes, V < k, bad dtype, max_depth, NULL, misaligned
         lambda: bd.spec_draft_tree(FAKE, bd.SPEC_BF16, 2, 160, 100, FAKE, FAKE, FAKE, 4, FAKE, 3, 0, FAKE, FAKE,
                                    FAKE, FAKE, stream=0),

@@ -1,0 +1,172 @@
+"""GPU parity of acceptance by probability (spec_prob_accept) against the oracle.
+
+Bars: the greedy tokens bit-exact; each node's target probability within a
+relative 2e-5 of the float64 softmax; the accepted lengths, paths and
+correction tokens bit-exact against the oracle's scan run on the kernel's own
+probabilities (the decisions are float32 comparisons on both sides); and the
+kernel's decisions equal the oracle's float64-based ones except for nodes
+whose probability sits within that tolerance of the decision boundary.  Soft
+matching's acceptance rate over seeded uniforms is checked against the
+target probability with a binomial bound.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from masked_verification_attention_amd import binding as bd
+from masked_verification_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+P_RTOL = 2e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def upload(a, dt=None):
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run(logits, dt, n_nodes, draft, parent, vrow, max_depth, mode, threshold=0.0, dprob=None, unif=None):
+    B, T, V = logits.shape
+    dev = dict(device="cuda")
+    am = torch.full((B, T), -9, dtype=torch.int32, **dev)
+    prob = torch.full((B, T), -9.0, dtype=torch.float32, **dev)
+    ln = torch.full((B,), -9, dtype=torch.int32, **dev)
+    pth = torch.full((B, max_depth), -9, dtype=torch.int32, **dev)
+    bonus = torch.full((B,), -9, dtype=torch.int32, **dev)
+    bd.spec_prob_accept(upload(logits, dt), bd.SPEC_BF16 if dt == "bf16" else bd.SPEC_F32, B, T, V,
+                        upload(n_nodes), upload(draft), upload(parent), None if vrow is None else upload(vrow),
+                        max_depth, mode, threshold, None if dprob is None else upload(dprob.astype(np.float32)),
+                        None if unif is None else upload(unif.astype(np.float32)), am, prob, ln, pth, bonus)
+    torch.cuda.synchronize()
+    return am.cpu().numpy(), prob.cpu().numpy(), ln.cpu().numpy(), pth.cpu().numpy(), bonus.cpu().numpy()
+
+
+def random_case(rng, B, T, V, dt, rows):
+    raw = rng.standard_normal((B, T, V)).astype(np.float32) * 2.0
+    draft = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    # a third of the drafts are the row's best or second-best token: probabilities span the range
+    for b in range(B):
+        for t in range(T):
+            r = rng.random()
+            if r < 0.35:
+                order = np.argsort(-raw[b, t])
+                draft[b, t] = order[0] if r < 0.2 else order[1]
+    parent = np.full((B, T), -1, dtype=np.int32)
+    for b in range(B):
+        for v in range(1, T):
+            parent[b, v] = int(rng.integers(-1, v)) if rows == "same" else int(rng.integers(0, v))
+    vrow = None
+    if rows == "parent":
+        # explicit root (node 0) and a parent's row verifying each child
+        vrow = parent.copy()
+        vrow[:, 0] = -1
+        # the drafts are read against the parent's row: re-draw the strong ones there
+        for b in range(B):
+            for v in range(1, T):
+                if rng.random() < 0.35:
+                    draft[b, v] = int(np.argmax(raw[b, parent[b, v]]))
+    data = wl.f32_to_bf16_bits(raw) if dt == "bf16" else raw
+    n_nodes = rng.integers(max(1, T - 3), T + 1, size=B).astype(np.int32)
+    return data, draft, parent, vrow, n_nodes
+
+
+def check(case_id, data, dt, n_nodes, draft, parent, vrow, max_depth, mode, threshold=0.0, dprob=None, unif=None):
+    am, prob, ln, pth, bonus = run(data, dt, n_nodes, draft, parent, vrow, max_depth, mode, threshold, dprob, unif)
+    greedy, p_ref, ok_ref, A_ref, path_ref, bonus_ref = oracle.prob_accept(
+        data, dt, n_nodes, draft, parent, vrow, max_depth, mode, threshold, dprob, unif)
+    B, T = draft.shape
+    band = 0
+    for b in range(B):
+        n = int(n_nodes[b])
+        np.testing.assert_array_equal(am[b, :n], greedy[b, :n])
+        assert (am[b, n:] == -1).all() and np.isnan(prob[b, n:]).all()
+        np.testing.assert_allclose(prob[b, :n], p_ref[b, :n], rtol=P_RTOL, atol=1e-30)
+    # the kernel's scan on its own probabilities: exact
+    _, _, ok_k, A_k, path_k, bonus_k = oracle.prob_accept(data, dt, n_nodes, draft, parent, vrow, max_depth, mode,
+                                                         threshold, dprob, unif, p=prob.astype(np.float64))
+    np.testing.assert_array_equal(ln, A_k)
+    np.testing.assert_array_equal(pth, path_k)
+    np.testing.assert_array_equal(bonus, bonus_k)
+    # decisions from float64 probabilities differ only next to the boundary
+    for b in range(B):
+        for v in range(int(n_nodes[b])):
+            if ok_k[b, v] != ok_ref[b, v]:
+                edge = threshold if mode == oracle.MODE_THRESHOLD else float(np.float32(unif[b, v]) *
+                                                                              np.float32(dprob[b, v]))
+                assert abs(p_ref[b, v] - edge) <= 2 * P_RTOL * max(abs(edge), 1e-30), (b, v)
+                band += 1
+    if band == 0:
+        np.testing.assert_array_equal(ln, A_ref)
+        np.testing.assert_array_equal(pth, path_ref)
+        np.testing.assert_array_equal(bonus, bonus_ref)
+    say(f"    {case_id}: accepted {ln.tolist()[:8]}, boundary nodes {band}")
+
+
+CASES = [
+    # (id, B, T, V, dtype, rows)
+    ("bf16_same_rows", 4, 30, 32000, "bf16", "same"),
+    ("bf16_parent_rows_llama", 3, 31, 128256, "bf16", "parent"),
+    ("f32_misaligned", 3, 12, 1003, "f32", "same"),
+    ("bf16_misaligned_parent", 3, 20, 1001, "bf16", "parent"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("mode", [oracle.MODE_THRESHOLD, oracle.MODE_SOFT], ids=["threshold", "soft"])
+def test_prob_accept_parity(case, mode):
+    cid, B, T, V, dt, rows = case
+    rng = np.random.default_rng(len(cid) * 100 + B * 10 + mode)
+    say(f"[gpu] prob accept {cid} mode {mode}")
+    data, draft, parent, vrow, n_nodes = random_case(rng, B, T, V, dt, rows)
+    if mode == oracle.MODE_THRESHOLD:
+        p = oracle.node_probs(data, dt, n_nodes, draft, vrow)
+        thr = float(np.nanmedian(p[p > 0])) if (p > 0).any() else 0.1
+        check(cid, data, dt, n_nodes, draft, parent, vrow, 8, mode, threshold=thr)
+        check(cid + "/t0", data, dt, n_nodes, draft, parent, vrow, 8, mode, threshold=0.0)
+    else:
+        dprob = rng.random((B, T)).astype(np.float32)
+        dprob[:, ::7] = 0.0
+        unif = rng.random((B, T)).astype(np.float32)
+        check(cid, data, dt, n_nodes, draft, parent, vrow, 8, mode, dprob=dprob, unif=unif)
+
+
+def test_soft_acceptance_rate_on_device():
+    # 4096 one-node requests over the same row: accepted iff u < p, so the rate is p
+    rng = np.random.default_rng(21)
+    B, V = 4096, 1000
+    row = (rng.standard_normal(V) * 2).astype(np.float32)
+    x = int(np.argsort(row)[-2])
+    logits = np.broadcast_to(row, (B, 1, V)).copy()
+    draft = np.full((B, 1), x, dtype=np.int32)
+    parent = np.full((B, 1), -1, dtype=np.int32)
+    n_nodes = np.ones(B, dtype=np.int32)
+    unif = rng.random((B, 1)).astype(np.float32)
+    _, prob, ln, _, _ = run(logits, "f32", n_nodes, draft, parent, None, 2, oracle.MODE_SOFT,
+                            dprob=np.ones((B, 1), np.float32), unif=unif)
+    pt = oracle.target_prob(row, "f32", x)
+    hits = int(ln.sum())
+    sd = np.sqrt(B * pt * (1 - pt))
+    say(f"    soft rate: p = {pt:.4f}, accepted {hits} of {B}")
+    assert abs(hits - B * pt) < 5 * sd
+    assert (ln == (unif[:, 0] < prob[:, 0])).all()
+
+
+def test_planted_workload_threshold():
+    # the ConFu-shaped workload's planted drafts (logit 8 over standard normal rows of
+    # 128256) carry probability ~0.01: a threshold of 1e-3 accepts them, 0.5 none
+    cfg = wl.CONFIGS["c3_confu_8b"]
+    x = wl.generate(cfg, B=4, L=(8, 8))
+    for thr in (1e-3, 0.5):
+        check(f"c3_planted/{thr}", x["logits"], "bf16", x["n_nodes"], x["draft_tok"], x["acc_parent"], None,
+              cfg.max_depth, oracle.MODE_THRESHOLD, threshold=thr)
