@@ -390,6 +390,20 @@ int spec_commit_kv(const spec_attn_desc* d, void* k_cache, void* v_cache,
                    const int32_t* out_len, const int32_t* out_path, int32_t max_depth,
                    void* stream);
 
+/*
+ * spec_argmax_accept_commit -- spec_argmax_accept_rows followed by
+ * spec_commit_kv of the accepted path, in two launches instead of three (the
+ * acceptance scan's workgroup copies its request's rows as soon as its path
+ * is known).  Same arguments, meanings and results as those two calls, with
+ * B taken from the descriptor; block row v holds node v (T <= d->Tq).
+ */
+int spec_argmax_accept_commit(const void* logits, int32_t logits_dtype, int32_t T, int32_t V, const int32_t* n_nodes,
+                              const int32_t* draft_tok, const int32_t* acc_parent, const int32_t* verify_row,
+                              int32_t max_depth, int32_t* out_argmax, int32_t* out_len, int32_t* out_path,
+                              int32_t* out_bonus, const spec_attn_desc* d, void* k_cache, void* v_cache,
+                              const int32_t* cache_len_in, int32_t* cache_len_out, const void* k_blk,
+                              const void* v_blk, void* stream);
+
 /* Static description of a status code. */
 const char* spec_strerror(int status);
 

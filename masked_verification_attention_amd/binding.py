@@ -35,7 +35,8 @@ SPEC_ACCEPT_SOFT = 2
 
 # every symbol the header declares
 EXPORTS = ("spec_build_mask", "spec_build_msa_mask", "spec_verify_attn_workspace", "spec_verify_attn",
-           "spec_argmax_accept", "spec_argmax_accept_rows", "spec_prob_accept", "spec_commit_kv", "spec_draft_tree",
+           "spec_argmax_accept", "spec_argmax_accept_rows", "spec_prob_accept", "spec_commit_kv",
+           "spec_argmax_accept_commit", "spec_draft_tree",
            "spec_strerror", "spec_last_error", "spec_version")
 
 
@@ -77,6 +78,9 @@ def load() -> ctypes.CDLL:
     lib.spec_prob_accept.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _P,
                                      _P, _P, _P, _P]
     lib.spec_prob_accept.restype = ctypes.c_int
+    lib.spec_argmax_accept_commit.argtypes = [_P, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P,
+                                              ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P, _P]
+    lib.spec_argmax_accept_commit.restype = ctypes.c_int
     lib.spec_verify_attn_workspace.argtypes = [ctypes.POINTER(AttnDesc)]
     lib.spec_verify_attn_workspace.restype = ctypes.c_size_t
     lib.spec_verify_attn.argtypes = [ctypes.POINTER(AttnDesc)] + [_P] * 14 + [ctypes.c_size_t, _P]
@@ -208,3 +212,15 @@ def spec_prob_accept(logits, logits_dtype, B, T, V, n_nodes, draft_tok, acc_pare
                                 _ptr(draft_prob), _ptr(uniform), _ptr(out_argmax), _ptr(out_prob), _ptr(out_len),
                                 _ptr(out_path), _ptr(out_bonus), _stream(stream) if B else None),
            "spec_prob_accept")
+
+
+def spec_argmax_accept_commit(logits, logits_dtype, T, V, n_nodes, draft_tok, acc_parent, verify_row, max_depth,
+                              out_argmax, out_len, out_path, out_bonus, desc: AttnDesc, k_cache, v_cache,
+                              cache_len_in, cache_len_out, k_blk, v_blk, stream=None):
+    lib = load()
+    _check(lib.spec_argmax_accept_commit(_ptr(logits), logits_dtype, T, V, _ptr(n_nodes), _ptr(draft_tok),
+                                         _ptr(acc_parent), _ptr(verify_row), max_depth, _ptr(out_argmax),
+                                         _ptr(out_len), _ptr(out_path), _ptr(out_bonus), ctypes.byref(desc),
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(cache_len_in), _ptr(cache_len_out),
+                                         _ptr(k_blk), _ptr(v_blk), _stream(stream) if desc.B else None),
+           "spec_argmax_accept_commit")

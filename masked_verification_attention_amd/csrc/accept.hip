@@ -33,6 +33,7 @@
 // scaled by the draft's own probability -- u * p_draft < p, i.e. acceptance
 // with probability min(1, p / p_draft) ("Speculative Streaming", soft
 // matching after Leviathan et al.).
+#include "commit_rows.hpp"
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -296,10 +297,12 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
                                                         const int32_t* __restrict__ argmax, int max_depth,
                                                         int32_t* __restrict__ out_len,
                                                         int32_t* __restrict__ out_path,
-                                                        int32_t* __restrict__ out_bonus, AcceptRule rule) {
+                                                        int32_t* __restrict__ out_bonus, AcceptRule rule,
+                                                        CommitArgs commit) {
   __shared__ int32_t par[SPEC_MAX_NODES];
   __shared__ uint8_t okv[SPEC_MAX_NODES];
   __shared__ float row_lse[SPEC_MAX_NODES];
+  __shared__ int32_t path_s[SPEC_MAX_DEPTH];
   __shared__ int red_i[kAccThreads / kWave];
   __shared__ uint64_t red_h[kAccThreads / kWave];
   __shared__ uint64_t red_l[kAccThreads / kWave];
@@ -432,6 +435,12 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
       node = (int)((w >> sh) & 0xffull);
     }
     out_path[(int64_t)b * max_depth + v] = node;
+    path_s[v] = node;
+  }
+  // fused form: append the accepted rows to the cache in the same launch
+  if (commit.enabled) {
+    __syncthreads();
+    commit_rows(b, commit, a_len, path_s);
   }
 }
 
@@ -462,9 +471,9 @@ hipError_t launch_argmax_lse(const void* logits, int dtype, int B, int T, int V,
 hipError_t launch_accept(int B, int T, const int32_t* n_nodes, const int32_t* draft_tok,
                          const int32_t* acc_parent, const int32_t* verify_row, const int32_t* argmax,
                          int max_depth, int32_t* out_len, int32_t* out_path, int32_t* out_bonus,
-                         const AcceptRule& rule, hipStream_t st) {
+                         const AcceptRule& rule, const CommitArgs& commit, hipStream_t st) {
   hipLaunchKernelGGL(k_accept, dim3(B), dim3(kAccThreads), 0, st, T, n_nodes, draft_tok, acc_parent, verify_row,
-                     argmax, max_depth, out_len, out_path, out_bonus, rule);
+                     argmax, max_depth, out_len, out_path, out_bonus, rule, commit);
   return hipGetLastError();
 }
 

@@ -150,8 +150,9 @@ int argmax_accept_impl(const char* fn, const void* logits, int32_t logits_dtype,
   hipError_t e = sv::launch_argmax(logits, logits_dtype, B, T, V, n_nodes, out_argmax, s);
   if (e != hipSuccess) return hip_status(e, "argmax launch");
   sv::AcceptRule greedy{};
+  sv::CommitArgs no_commit{};
   e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, verify_row, out_argmax, max_depth, out_len,
-                        out_path, out_bonus, greedy, s);
+                        out_path, out_bonus, greedy, no_commit, s);
   return hip_status(e, "acceptance scan launch");
 }
 
@@ -283,8 +284,9 @@ int spec_prob_accept(const void* logits, int32_t logits_dtype, int32_t B, int32_
   rule.logits_bf16 = logits_dtype == SPEC_BF16;
   rule.V = V;
   rule.prob = out_prob;
+  sv::CommitArgs no_commit{};
   e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, verify_row, out_argmax, max_depth, out_len, out_path,
-                        out_bonus, rule, s);
+                        out_bonus, rule, no_commit, s);
   return hip_status(e, "acceptance scan launch");
 }
 
@@ -406,6 +408,46 @@ int spec_commit_kv(const spec_attn_desc* d, void* k_cache, void* v_cache, const 
                         d->kv_stride_l, d->kv_stride_h, k_cache, v_cache, cache_len_in, cache_len_out, k_blk,
                         v_blk, out_len, out_path, max_depth, static_cast<hipStream_t>(stream));
   return hip_status(e, "spec_commit_kv launch");
+}
+
+int spec_argmax_accept_commit(const void* logits, int32_t logits_dtype, int32_t T, int32_t V, const int32_t* n_nodes,
+                              const int32_t* draft_tok, const int32_t* acc_parent, const int32_t* verify_row,
+                              int32_t max_depth, int32_t* out_argmax, int32_t* out_len, int32_t* out_path,
+                              int32_t* out_bonus, const spec_attn_desc* d, void* k_cache, void* v_cache,
+                              const int32_t* cache_len_in, int32_t* cache_len_out, const void* k_blk,
+                              const void* v_blk, void* stream) {
+  const int st = check_desc(d);
+  if (st != SPEC_OK) return st;
+  const int B = d->B;
+  REQUIRE(T >= 1 && T <= SPEC_MAX_NODES, SPEC_EINVAL, "T = %d outside [1, %d]", T, SPEC_MAX_NODES);
+  REQUIRE(T <= d->Tq, SPEC_EINVAL, "T = %d acceptance nodes exceed the block's Tq = %d rows", T, d->Tq);
+  REQUIRE(V >= 1, SPEC_EINVAL, "V = %d < 1", V);
+  REQUIRE(max_depth >= 1 && max_depth <= SPEC_MAX_DEPTH, SPEC_EINVAL, "max_depth = %d outside [1, %d]", max_depth,
+          SPEC_MAX_DEPTH);
+  REQUIRE(logits_dtype == SPEC_F32 || logits_dtype == SPEC_BF16, SPEC_EINVAL, "logits_dtype = %d is not a spec_dtype",
+          logits_dtype);
+  REQUIRE((int64_t)B * T <= 0x7fffffff, SPEC_EUNSUPPORTED, "B * T too large");
+  if (B == 0) return ok();
+  REQUIRE(logits && n_nodes && draft_tok && acc_parent && out_argmax && out_len && out_path && k_cache && v_cache &&
+              cache_len_in && cache_len_out && k_blk && v_blk,
+          SPEC_EINVAL, "all array arguments except verify_row and out_bonus must be non-NULL");
+  REQUIRE(aligned(logits, esize_of(logits_dtype)), SPEC_EINVAL, "logits must be aligned to its element size");
+  REQUIRE(aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(k_blk, 16) && aligned(v_blk, 16), SPEC_EINVAL,
+          "caches and block must be 16-byte aligned");
+  REQUIRE(aligned(n_nodes, 4) && aligned(draft_tok, 4) && aligned(acc_parent, 4) && aligned(verify_row, 4) &&
+              aligned(out_argmax, 4) && aligned(out_len, 4) && aligned(out_path, 4) && aligned(out_bonus, 4) &&
+              aligned(cache_len_in, 4) && aligned(cache_len_out, 4),
+          SPEC_EINVAL, "int32 arrays must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = sv::launch_argmax(logits, logits_dtype, B, T, V, n_nodes, out_argmax, s);
+  if (e != hipSuccess) return hip_status(e, "argmax launch");
+  sv::AcceptRule greedy{};
+  sv::CommitArgs c{1, d->Tq, d->Hkv, d->D, esize_of(d->dtype), d->lmax, d->kv_stride_b, d->kv_stride_l,
+                   d->kv_stride_h, static_cast<char*>(k_cache), static_cast<char*>(v_cache), cache_len_in,
+                   cache_len_out, static_cast<const char*>(k_blk), static_cast<const char*>(v_blk)};
+  e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, verify_row, out_argmax, max_depth, out_len, out_path,
+                        out_bonus, greedy, c, s);
+  return hip_status(e, "acceptance + commit launch");
 }
 
 }  // extern "C"

@@ -66,6 +66,19 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t st);
 hipError_t launch_argmax(const void* logits, int dtype, int B, int T, int V, const int32_t* n_nodes,
                          int32_t* out_argmax, hipStream_t st);
+// Cache commit of an accepted path (k_commit, or fused after the acceptance scan).
+struct CommitArgs {
+  int enabled;              // fused form: 0 = acceptance only
+  int Tq, Hkv, D, esize;
+  int64_t lmax, sb, sl, sh; // cache capacity and element strides
+  char* k_cache;
+  char* v_cache;
+  const int32_t* cache_len_in;
+  int32_t* cache_len_out;
+  const char* k_blk;
+  const char* v_blk;
+};
+
 // Per-node acceptance decision of k_accept.
 struct AcceptRule {
   int mode;                 // 0: the draft equals the row's greedy token; 1: p > threshold; 2: u * p_draft < p
@@ -84,7 +97,7 @@ hipError_t launch_argmax_lse(const void* logits, int dtype, int B, int T, int V,
 hipError_t launch_accept(int B, int T, const int32_t* n_nodes, const int32_t* draft_tok,
                          const int32_t* acc_parent, const int32_t* verify_row, const int32_t* argmax,
                          int max_depth, int32_t* out_len, int32_t* out_path, int32_t* out_bonus,
-                         const AcceptRule& rule, hipStream_t st);
+                         const AcceptRule& rule, const CommitArgs& commit, hipStream_t st);
 hipError_t launch_commit(int B, int Tq, int Hkv, int D, int esize, int64_t lmax, int64_t sb,
                          int64_t sl, int64_t sh, void* k_cache, void* v_cache,
                          const int32_t* cache_len_in, int32_t* cache_len_out, const void* k_blk,

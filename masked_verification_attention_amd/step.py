@@ -2,9 +2,10 @@
 
 Uploads one seeded workload (``workloads.generate``) to HBM as torch tensors,
 allocates every output, and runs the four entry points on one stream:
-spec_build_mask -> spec_verify_attn -> spec_argmax_accept -> spec_commit_kv
-(multi-stream workloads: spec_build_msa_mask, spec_argmax_accept_rows and
-spec_draft_tree for the next draft).
+spec_build_mask -> spec_verify_attn -> spec_argmax_accept_commit (the fused
+form of spec_argmax_accept + spec_commit_kv, which are also exposed); multi-
+stream workloads use spec_build_msa_mask, verification rows and
+spec_draft_tree for the next draft.
 This module only moves memory and marshals arguments; all arithmetic runs in
 the HIP kernels.  torch supplies the device memory and the stream.
 """
@@ -158,6 +159,16 @@ class VerifyStep:
                           self.cache_len if in_place else self.cache_len_out, self.k_blk, self.v_blk,
                           self.out_len, self.out_path, self.max_depth, stream)
 
+    def accept_commit(self, stream=None, in_place=False):
+        """Argmax, acceptance and commit in two launches (spec_argmax_accept_commit); multi-stream
+        workloads verify each node against its parent's row and return the correction token."""
+        bd.spec_argmax_accept_commit(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.T, self.V, self.n_nodes,
+                                     self.draft_tok, self.acc_parent, self.acc_parent if self.msa else None,
+                                     self.max_depth, self.argmax, self.out_len, self.out_path, self.out_bonus,
+                                     self.desc, self.k_cache, self.v_cache, self.cache_len,
+                                     self.cache_len if in_place else self.cache_len_out, self.k_blk, self.v_blk,
+                                     stream)
+
     def draft(self, stream=None):
         """The next tree draft from the new root's speculative streams (multi-stream workloads)."""
         bd.spec_draft_tree(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.Tq, self.V, self.n_nodes,
@@ -169,7 +180,6 @@ class VerifyStep:
         multi-stream workloads also draft the next tree in the same pass."""
         self.build_mask(stream)
         self.attention(stream)
-        self.argmax_accept(stream)
-        self.commit(stream)
+        self.accept_commit(stream)
         if self.msa:
             self.draft(stream)

@@ -108,6 +108,8 @@ def test_empty_batch_is_a_noop_without_touching_memory():
     attn(good_desc(B=0), q=None, out=None)
     bd.spec_build_mask(None, None, None, 0, 8, None, None, stream=0)
     bd.spec_build_msa_mask(None, None, 0, 40, 3, 160, None, None, None, stream=0)
+    bd.spec_argmax_accept_commit(None, bd.SPEC_BF16, 4, 100, None, None, None, None, 4, None, None, None, None,
+                                 good_desc(B=0), None, None, None, None, None, None, stream=0)
     bd.spec_prob_accept(None, bd.SPEC_BF16, 0, 4, 100, None, None, None, None, 4, bd.SPEC_ACCEPT_SOFT, 0.0, None,
                         None, None, None, None, None, None, stream=0)
     bd.spec_draft_tree(None, bd.SPEC_BF16, 0, 160, 100, None, None, None, 4, None, 3, 3, None, None, None, None,
@@ -144,6 +146,19 @@ def test_other_entry_points_reject_bad_arguments():
                                     bd.SPEC_ACCEPT_THRESHOLD, 0.5, None, None, FAKE, FAKE, FAKE, FAKE, None, stream=0),
         lambda: bd.spec_prob_accept(FAKE, bd.SPEC_BF16, 2, 4, 100, FAKE, FAKE, FAKE, None, 4, bd.SPEC_ACCEPT_SOFT,
                                     0.0, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, stream=0),
+        # spec_argmax_accept_commit: T over the block, bad descriptor, NULL cache, misaligned block
+        lambda: bd.spec_argmax_accept_commit(FAKE, bd.SPEC_BF16, 64, 100, FAKE, FAKE, FAKE, None, 4, FAKE, FAKE,
+                                             FAKE, None, good_desc(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept_commit(FAKE, bd.SPEC_BF16, 4, 100, FAKE, FAKE, FAKE, None, 4, FAKE, FAKE,
+                                             FAKE, None, good_desc(D=80), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                             stream=0),
+        lambda: bd.spec_argmax_accept_commit(FAKE, bd.SPEC_BF16, 4, 100, FAKE, FAKE, FAKE, None, 4, FAKE, FAKE,
+                                             FAKE, None, good_desc(), None, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
+        lambda: bd.spec_argmax_accept_commit(FAKE, bd.SPEC_BF16, 4, 100, FAKE, FAKE, FAKE, None, 4, FAKE, FAKE,
+                                             FAKE, None, good_desc(), FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE,
+                                             stream=0),
+        lambda: bd.spec_argmax_accept_commit(FAKE, bd.SPEC_BF16, 4, 100, FAKE, FAKE, FAKE, None, 17, FAKE, FAKE,
+                                             FAKE, None, good_desc(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
         # spec_draft_tree: k out of range, tree over 256 nodes, V < k, bad dtype, max_depth, NULL, misaligned
         lambda: bd.spec_draft_tree(FAKE, bd.SPEC_BF16, 2, 160, 100, FAKE, FAKE, FAKE, 4, FAKE, 3, 0, FAKE, FAKE,
                                    FAKE, FAKE, stream=0),

@@ -372,3 +372,35 @@ def test_full_size_sampled(name):
             np.testing.assert_array_equal(v_host[b, L[b] + d], x["v_blk"][b, path[b, d]])
         np.testing.assert_array_equal(k_host[b, :L[b]], x["k_cache"][b, :L[b]])
     say(f"    accepted lengths {A.tolist()}")
+
+
+@pytest.mark.parametrize("name", ["c1_tiny_la", "c2_la_7b", "c3_confu_8b", "c4_tree_3b", "c5_stream_70b",
+                                  "c6_msa_1b"])
+def test_fused_accept_commit_matches_oracle(name):
+    # spec_argmax_accept_commit: the same results as acceptance then commit, in two launches
+    cfg = wl.CONFIGS[name]
+    say(f"[gpu] fused accept+commit {name}")
+    x = wl.generate(cfg, B=min(cfg.B, 3), L=(40, 90) if cfg.L[0] else None)
+    st = VerifyStep(cfg, x)
+    # request 0 has room for one row only: the capacity rule applies in the fused form too
+    st.cache_len.copy_(torch.tensor([st.lmax - 1] + [int(v) for v in x["cache_len"][1:]], dtype=torch.int32))
+    st.accept_commit()
+    torch.cuda.synchronize()
+    L0 = np.array([st.lmax - 1] + list(x["cache_len"][1:]), dtype=np.int32)
+    if cfg.structure == "msa_tree":
+        B, T = x["acc_parent"].shape
+        vrow = x["acc_parent"].copy()             # nodes first: a parent's node index is its main row
+        _, A, path, _, bonus = oracle.argmax_accept_rows(x["logits"], cfg.logits_dtype, x["n_nodes"],
+                                                         x["draft_tok"], x["acc_parent"], vrow, st.max_depth)
+        np.testing.assert_array_equal(st.out_bonus.cpu().numpy(), bonus)
+    else:
+        _, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                          x["acc_parent"], st.max_depth)
+    np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
+    np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
+    kc, vc, L2 = oracle.commit_kv(x["k_cache"], x["v_cache"], L0, x["k_blk"], x["v_blk"], A, path)
+    np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L2)
+    k_host, v_host = st.cache_host()
+    np.testing.assert_array_equal(k_host, kc)
+    np.testing.assert_array_equal(v_host, vc)
+    say(f"    accepted {A.tolist()}, new lengths {L2.tolist()}")
