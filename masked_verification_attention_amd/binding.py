@@ -68,6 +68,10 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m masked_verification_attention_amd.build` (there is no CPU fallback)")
+    # torch ships its own HIP runtime under the same soname; loading torch first makes the
+    # library bind to that one, so that torch's streams and ours belong to a single runtime
+    # (loaded the other way round, the process would hold two runtimes)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     lib.spec_build_mask.argtypes = [_P, _P, _P, _I, _I, _P, _P, _P]
     lib.spec_build_mask.restype = ctypes.c_int
