@@ -105,9 +105,9 @@ class VerifyConfig:
         return replace(self, **kw)
 
 
-# The five workloads (C1..C5).  Values not fixed by the workload descriptions
-# are the readings recorded in the design notes: C3 accept probability 0.8,
-# C4 soft rows 16 and depth cap 6, C5 as 32 fixed chains of 4.
+# The workloads (C1..C5 here, C6 below).  Values the workload descriptions
+# leave open are readings: C3 accept probability 0.8, C4 soft rows 16 and
+# depth cap 6, C5 as 32 fixed chains of 4.
 CONFIGS: Dict[str, VerifyConfig] = {
     "c1_tiny_la": VerifyConfig(
         name="c1_tiny_la", B=1, Hq=2, Hkv=2, D=64, dtype="f32", L=(128, 128), S=0,
