@@ -9,12 +9,18 @@
  * as hand-written HIP kernels:
  *
  *   spec_build_mask     parent array -> bit-packed block visibility mask
+ *   spec_build_msa_mask the same for multi-stream rows (main + speculative
+ *                       streams per tree node)
  *   spec_verify_attn    attention of the block's queries over
  *                       [soft prompt | cached prefix | block] under that mask
  *   spec_argmax_accept  per-node greedy token, longest accepted path
  *   spec_argmax_accept_rows  the same with explicit verification rows, an
  *                       explicit root and the correction token
+ *   spec_prob_accept    the same scan with a threshold or soft-matching rule
+ *                       on the target's probability of each draft
  *   spec_commit_kv      append the accepted nodes' K/V to the cache
+ *   spec_argmax_accept_commit  argmax, acceptance and commit, fused
+ *   spec_draft_tree     the next tree draft from the new root's streams
  *
  * Sources (page titles; sections, equations):
  *   [LA] "Lookahead Attention: Self-Speculative Verification via Parallel
@@ -24,10 +30,12 @@
  *        key design 1: soft prompt in the KV cache visible only to
  *        contemplate tokens; one contemplate token per tree node (2T rows).
  *   [SS] "Speculative Streaming: Fast LLM Inference without Auxiliary
- *        Models" -- Equation 1 (attention, 1/sqrt(d) scale), tree draft and
- *        Equation 4 (each node sees its root-to-node path), the verification
- *        step (depth-first, hard matching, longest accepted path), lazy KV
- *        garbage collection after the step.
+ *        Models" -- Equation 1 (attention, 1/sqrt(d) scale), Equation 2
+ *        (multi-stream attention), tree draft construction and Equation 4
+ *        (each node sees its root-to-node path), batching with speculative
+ *        streams, the verification step (depth-first, hard or soft matching,
+ *        longest accepted path, correction token), parallel new draft
+ *        generation, lazy KV garbage collection after the step.
  *
  * Conventions (all entry points):
  *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
