@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets cycled between steps (0: enough for ~1 GB, at least 3)")
     ap.add_argument("--workload", choices=sorted(DESCRIPTIONS), default=WORKLOAD)
+    ap.add_argument("--accept", choices=("greedy", "threshold", "soft"), default="greedy",
+                    help="acceptance rule of the step (greedy: hard matching, fused with the commit)")
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0)
@@ -254,7 +256,14 @@ def main():
         args.sets = int(min(16, max(3, np.ceil(1e9 / wl.nbytes_of(first)))))
     for i in range(args.sets):
         x = first if i == 0 else wl.generate(cfg, seed=cfg.seed + 100 * i)
-        st = VerifyStep(cfg, x, device="cuda:0", kv_splits=args.kv_splits, layout=args.layout)
+        # probability rules: the draft's own probability and the uniform draw are inputs
+        # (seeded here, as a caller's generator would supply them)
+        urng = np.random.default_rng(cfg.seed + 7 + i)
+        T_acc = x["acc_parent"].shape[1]
+        st = VerifyStep(cfg, x, device="cuda:0", kv_splits=args.kv_splits, layout=args.layout,
+                        accept=args.accept, threshold=1e-3,
+                        draft_prob=urng.random((cfg.B, T_acc)).astype(np.float32) * 0.02,
+                        uniform=urng.random((cfg.B, T_acc)).astype(np.float32))
         steps_state.append((st, x))
     torch.cuda.synchronize()
     log(f"inputs: {args.sets} sets generated and uploaded in {time.time() - t0:.1f}s")
@@ -317,7 +326,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload][0],
                    "global_batch": cfg.B, "seq_len": DESCRIPTIONS[args.workload][1], "query_rows": cfg.Tq,
-                   "kv_layout": args.layout,
+                   "kv_layout": args.layout, "acceptance": args.accept,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": counters_traffic(args.workload),

@@ -48,11 +48,15 @@ class VerifyStep:
     """One verification step's device state for a workload."""
 
     def __init__(self, cfg: VerifyConfig, x: Dict[str, np.ndarray], device="cuda", kv_splits: int = 0,
-                 scale: float = 0.0, max_depth: Optional[int] = None, layout: str = "blhd"):
+                 scale: float = 0.0, max_depth: Optional[int] = None, layout: str = "blhd",
+                 accept: str = "greedy", threshold: float = 1e-3, draft_prob=None, uniform=None):
         """``layout`` of the K/V cache in HBM: "blhd" = [B, lmax, Hkv, D] (token-major, the
         generator's order) or "bhld" = [B, Hkv, lmax, D] (head-major).  Both are passed to
         the library through the descriptor's strides; ``cache_host()`` returns the
-        cache in the generator's order either way."""
+        cache in the generator's order either way.  ``accept`` selects the acceptance rule
+        of ``run()``: "greedy" (hard matching), "threshold" (target probability above
+        ``threshold``) or "soft" (soft matching with the given ``draft_prob`` and
+        ``uniform`` arrays [B, T])."""
         self.cfg = cfg
         self.device = torch.device(device)
         dt = cfg.dtype
@@ -100,6 +104,16 @@ class VerifyStep:
         self.out_len = torch.empty(self.B, **i32)
         self.out_path = torch.empty(self.B, self.max_depth, **i32)
         self.out_bonus = torch.empty(self.B, **i32)
+        if accept not in ("greedy", "threshold", "soft"):
+            raise ValueError(accept)
+        self.accept, self.threshold = accept, float(threshold)
+        self.out_prob = torch.empty(self.B, self.T, dtype=torch.float32, device=dev)
+        self.draft_prob = self.uniform = None
+        if accept == "soft":
+            if draft_prob is None or uniform is None:
+                raise ValueError("soft matching needs draft_prob and uniform")
+            self.draft_prob = to_device(np.asarray(draft_prob, np.float32), "f32", dev)
+            self.uniform = to_device(np.asarray(uniform, np.float32), "f32", dev)
         if self.msa:
             # the next draft: k tokens per stream of the new root, a complete k-ary tree
             k, g = cfg.branch, cfg.gamma
@@ -169,6 +183,14 @@ class VerifyStep:
                                      self.cache_len if in_place else self.cache_len_out, self.k_blk, self.v_blk,
                                      stream)
 
+    def prob_accept(self, stream=None):
+        """Acceptance by the target's probability of each draft (spec_prob_accept)."""
+        mode = bd.SPEC_ACCEPT_THRESHOLD if self.accept == "threshold" else bd.SPEC_ACCEPT_SOFT
+        bd.spec_prob_accept(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.T, self.V, self.n_nodes,
+                            self.draft_tok, self.acc_parent, self.acc_parent if self.msa else None,
+                            self.max_depth, mode, self.threshold, self.draft_prob, self.uniform, self.argmax,
+                            self.out_prob, self.out_len, self.out_path, self.out_bonus, stream)
+
     def draft(self, stream=None):
         """The next tree draft from the new root's speculative streams (multi-stream workloads)."""
         bd.spec_draft_tree(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.Tq, self.V, self.n_nodes,
@@ -180,6 +202,10 @@ class VerifyStep:
         multi-stream workloads also draft the next tree in the same pass."""
         self.build_mask(stream)
         self.attention(stream)
-        self.accept_commit(stream)
+        if self.accept == "greedy":
+            self.accept_commit(stream)
+        else:
+            self.prob_accept(stream)
+            self.commit(stream)
         if self.msa:
             self.draft(stream)

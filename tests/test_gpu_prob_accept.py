@@ -170,3 +170,32 @@ def test_planted_workload_threshold():
     for thr in (1e-3, 0.5):
         check(f"c3_planted/{thr}", x["logits"], "bf16", x["n_nodes"], x["draft_tok"], x["acc_parent"], None,
               cfg.max_depth, oracle.MODE_THRESHOLD, threshold=thr)
+
+
+@pytest.mark.parametrize("rule", ["threshold", "soft"])
+def test_step_with_probability_acceptance(rule):
+    # the whole step (mask, attention, probability acceptance, commit) as the benchmark runs it
+    from masked_verification_attention_amd.step import VerifyStep
+    cfg = wl.CONFIGS["c3_confu_8b"]
+    x = wl.generate(cfg, B=3, L=(40, 80))
+    rng = np.random.default_rng(5)
+    dprob = (rng.random(x["acc_parent"].shape) * 0.02).astype(np.float32)
+    unif = rng.random(x["acc_parent"].shape).astype(np.float32)
+    st = VerifyStep(cfg, x, accept=rule, threshold=1e-3, draft_prob=dprob, uniform=unif)
+    st.run()
+    torch.cuda.synchronize()
+    mode = oracle.MODE_THRESHOLD if rule == "threshold" else oracle.MODE_SOFT
+    prob = st.out_prob.cpu().numpy().astype(np.float64)
+    _, p_ref, _, _, _, _ = oracle.prob_accept(x["logits"], "bf16", x["n_nodes"], x["draft_tok"], x["acc_parent"],
+                                              None, st.max_depth, mode, 1e-3, dprob, unif)
+    np.testing.assert_allclose(prob, p_ref, rtol=P_RTOL, atol=1e-30)
+    _, _, _, A, path, _ = oracle.prob_accept(x["logits"], "bf16", x["n_nodes"], x["draft_tok"], x["acc_parent"],
+                                             None, st.max_depth, mode, 1e-3, dprob, unif, p=prob)
+    np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
+    np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
+    kc, vc, L2 = oracle.commit_kv(x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"], A, path)
+    np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L2)
+    k_host, v_host = st.cache_host()
+    np.testing.assert_array_equal(k_host, kc)
+    np.testing.assert_array_equal(v_host, vc)
+    say(f"    {rule}: accepted {A.tolist()}")
