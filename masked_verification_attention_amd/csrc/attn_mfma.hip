@@ -53,7 +53,9 @@
 // rescaled; probabilities stay below 2^8, far from fp32 / bf16 limits.  The
 // common path does not even compute the tile max: the probabilities against
 // the current max are needed anyway, and their sum exceeds 2^8 whenever one of
-// them could.
+// them could.  Whether a row rescales is decided by that row alone, so each
+// query row's output is bitwise the same whatever the other rows of the
+// workgroup are (their K/V, their masks, or whether they exist).
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -380,11 +382,15 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       }
       pf[nb] = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
     };
-    // exact max of row block nb over xs, rescale its state, and recompute p
-    auto rescale = [&](int nb, const float (&xs)[8], float (&p)[8], float& ps) __attribute__((always_inline)) {
+    // Rescale row block nb and recompute p.  The new reference is the max over
+    // the lanes of the row that asked for it (need): a lane whose sum is within
+    // the bound stays within it against any larger reference.  A row that asked
+    // for nothing keeps its reference, so one row's arithmetic never depends on
+    // the other rows of its wave (the call is wave-uniform, the decision is not).
+    auto rescale = [&](int nb, const float (&xs)[8], float (&p)[8], float& ps, bool need) __attribute__((always_inline)) {
       const float lmax = fmaxf(fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3])),
                                fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7])));
-      float mx = lmax * a.c;
+      float mx = need ? lmax * a.c : -INFINITY;
       mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(lx16, __float_as_int(mx))));
       mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(lx32, __float_as_int(mx))));
       const float mnew = fmaxf(mrun[nb], mx);
@@ -401,10 +407,12 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     };
     // softmax of a complete prefix tile: no mask; probabilities against the current
-    // max, whose sum exceeds 2^TAU whenever one of them could (then rescale exactly)
-    auto softmax_full = [&](bool first) __attribute__((always_inline)) {
+    // max, whose sum exceeds 2^TAU whenever one of them could (then rescale exactly).
+    // check_empty: a row with no reference yet (no visible key so far) takes one;
+    // the hot steps pass false, as every row has one after its group's first tile.
+    auto softmax_full = [&](bool check_empty) __attribute__((always_inline)) {
       float xs[NB][8], p[NB][8], ps[NB];
-      bool need = first;
+      bool need[NB], any_need = false;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -413,11 +421,12 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
           p[nb][e] = fast_exp2(fmaf(xs[nb][e], a.c, negm[nb]));
         }
         ps[nb] = ((p[nb][0] + p[nb][1]) + (p[nb][2] + p[nb][3])) + ((p[nb][4] + p[nb][5]) + (p[nb][6] + p[nb][7]));
-        need = need || !(ps[nb] <= P_LIMIT);
+        need[nb] = (check_empty && mrun[nb] == -INFINITY) || !(ps[nb] <= P_LIMIT);
+        any_need = any_need || need[nb];
       }
-      if (__any(need)) {
+      if (__any(any_need)) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) rescale(nb, xs[nb], p[nb], ps[nb]);
+        for (int nb = 0; nb < NB; ++nb) rescale(nb, xs[nb], p[nb], ps[nb], need[nb]);
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -449,7 +458,8 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
           p[e] = fast_exp2(fmaf(xs[e], a.c, negm[nb]));
         }
         float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        if (__any(!(ps <= P_LIMIT) || mrun[nb] == -INFINITY)) rescale(nb, xs, p, ps);
+        const bool need = !(ps <= P_LIMIT) || mrun[nb] == -INFINITY;
+        if (__any(need)) rescale(nb, xs, p, ps, need);
         lrun[nb] += ps;
         pack(nb, p);
       }
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       else if (seg == 1) lim = min(C::TK, a.S - (t - ntp) * C::TK);
       else lim = min(C::TK, nq - (t - ntp - nts) * C::TK);
       if (seg == 0 && lim == C::TK)
-        softmax_full(mrun[0] == -INFINITY || (NB > 1 && mrun[NB - 1] == -INFINITY));
+        softmax_full(true);
       else
         softmax_masked(t, seg, lim);
     };

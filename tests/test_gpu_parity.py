@@ -206,6 +206,32 @@ def test_invisible_keys_do_not_change_outputs_bitwise():
     assert not torch.equal(st.out[:, T:], base[:, T:])
 
 
+@pytest.mark.parametrize("name", ["c3_confu_8b", "c4_tree_3b"])
+def test_truncated_block_leaves_earlier_rows_bitwise(name):
+    """Parents precede children, so cutting a request's block after row n' leaves
+    what rows < n' see unchanged; their outputs must not move by a single bit
+    although the rows sharing their waves and the block's tile count change."""
+    cfg = wl.CONFIGS[name]
+    x = wl.generate(cfg, B=3, L=(300, 500), with_logits=False)
+    st = VerifyStep(cfg, x)
+    st.build_mask()
+    st.attention()
+    torch.cuda.synchronize()
+    base = st.out.clone()
+    base_lse = st.lse.clone()
+    full = x["n_q"].copy()
+    cut = np.array([max(1, int(full[0]) // 2), 1, max(1, int(full[2]) - 33)], dtype=np.int32)
+    say(f"{name}: n_q {full.tolist()} -> {cut.tolist()}")
+    st.n_q.copy_(torch.from_numpy(cut))
+    st.build_mask()
+    st.attention()
+    torch.cuda.synchronize()
+    for b in range(3):
+        n = int(cut[b])
+        assert torch.equal(st.out[b, :n], base[b, :n]), (b, n)
+        assert torch.equal(st.lse[b, :n], base_lse[b, :n]), (b, n)
+
+
 @pytest.mark.parametrize("name", ["c1_tiny_la", "c2_la_7b", "c3_confu_8b", "c4_tree_3b", "c5_stream_70b"])
 def test_argmax_accept_and_commit_small(name):
     cfg = wl.CONFIGS[name]
