@@ -80,23 +80,12 @@ __device__ __forceinline__ void scan16(float& bv, int& bi, const u32x4& x, int i
   }
 }
 
+// First maximum of one logit row by the whole workgroup; the index is valid
+// in thread 0.
 template <typename T>
-__global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ logits, int T_, int V,
-                                                        const int32_t* __restrict__ n_nodes,
-                                                        int32_t* __restrict__ out) {
+__device__ __forceinline__ int row_argmax(const T* __restrict__ base, int V, float* sv_, int* si_) {
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
   constexpr int U = 8;               // 16-byte loads in flight per thread
-  __shared__ float sv_[kArgThreads / kWave];
-  __shared__ int si_[kArgThreads / kWave];
-  const int row = blockIdx.x;
-  const int b = row / T_;
-  const int v = row % T_;
-  const int n = clampi(n_nodes[b], 0, T_);
-  if (v >= n) {
-    if (threadIdx.x == 0) out[row] = -1;
-    return;
-  }
-  const T* base = logits + (int64_t)row * V;
   const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
   const int pre = min(V, mis == 0 ? 0 : E - mis);
   // two independent running maxima (even / odd load slots) shorten the dependency chain
@@ -154,9 +143,27 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ lo
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kArgThreads / kWave; ++w) better(bv, bi, sv_[w], si_[w]);
-    // a row of -inf only: every element ties, the first index wins
-    out[row] = bi == 0x7fffffff ? 0 : bi;
   }
+  // a row of -inf only: every element ties, the first index wins
+  return bi == 0x7fffffff ? 0 : bi;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ logits, int T_, int V,
+                                                        const int32_t* __restrict__ n_nodes,
+                                                        int32_t* __restrict__ out) {
+  __shared__ float sv_[kArgThreads / kWave];
+  __shared__ int si_[kArgThreads / kWave];
+  const int row = blockIdx.x;
+  const int b = row / T_;
+  const int v = row % T_;
+  const int n = clampi(n_nodes[b], 0, T_);
+  if (v >= n) {
+    if (threadIdx.x == 0) out[row] = -1;
+    return;
+  }
+  const int bi = row_argmax<T>(logits + (int64_t)row * V, V, sv_, si_);
+  if (threadIdx.x == 0) out[row] = bi;
 }
 
 // k_argmax_lse: the greedy token and the log-sum-exp of every node row, for
@@ -290,41 +297,52 @@ __device__ __forceinline__ bool key_less(uint64_t ah, uint64_t al, uint64_t bh, 
   return ah < bh || (ah == bh && al < bl);
 }
 
-__global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* __restrict__ n_nodes,
-                                                        const int32_t* __restrict__ draft_tok,
-                                                        const int32_t* __restrict__ acc_parent,
-                                                        const int32_t* __restrict__ verify_row,
-                                                        const int32_t* __restrict__ argmax, int max_depth,
-                                                        int32_t* __restrict__ out_len,
-                                                        int32_t* __restrict__ out_path,
-                                                        int32_t* __restrict__ out_bonus, AcceptRule rule,
-                                                        CommitArgs commit) {
-  __shared__ int32_t par[SPEC_MAX_NODES];
-  __shared__ uint8_t okv[SPEC_MAX_NODES];
-  __shared__ float row_lse[SPEC_MAX_NODES];
-  __shared__ int32_t path_s[SPEC_MAX_DEPTH];
-  __shared__ int red_i[kAccThreads / kWave];
-  __shared__ uint64_t red_h[kAccThreads / kWave];
-  __shared__ uint64_t red_l[kAccThreads / kWave];
-  __shared__ uint8_t lists[kAccThreads][SPEC_MAX_DEPTH];
-  const int b = blockIdx.x;
+// LDS of one request's acceptance scan
+struct AcceptSmem {
+  int32_t par[SPEC_MAX_NODES];
+  uint8_t okv[SPEC_MAX_NODES];
+  float row_lse[SPEC_MAX_NODES];
+  int32_t path_s[SPEC_MAX_DEPTH];
+  int red_i[kAccThreads / kWave];
+  uint64_t red_h[kAccThreads / kWave];
+  uint64_t red_l[kAccThreads / kWave];
+  uint8_t lists[kAccThreads][SPEC_MAX_DEPTH];
+};
+
+// The acceptance scan (and, when enabled, the commit) of request b by one
+// workgroup of kAccThreads threads, one per node.
+__device__ __forceinline__ void accept_request(AcceptSmem& sm, int b, int T_, const int32_t* n_nodes,
+                                               const int32_t* draft_tok, const int32_t* acc_parent,
+                                               const int32_t* verify_row, const int32_t* argmax, int max_depth,
+                                               int32_t* out_len, int32_t* out_path, int32_t* out_bonus,
+                                               const AcceptRule& rule, const CommitArgs& commit) {
   const int v = threadIdx.x;
-  const int n = clampi(n_nodes[b], 0, T_);
   const int wave = v / kWave;
   const int lane = v % kWave;
+  // Every load that does not depend on another goes out first, in one round
+  // trip: the node count, the cache length the commit appends at, and the
+  // node's parent, draft and (for its own row) greedy token.
+  const int n = clampi(n_nodes[b], 0, T_);
+  const int64_t len_in = commit.enabled ? commit.cache_len_in[b] : 0;
+  int par_v = -1, x = -1, u = v, g_own = -1;
+  if (v < T_) {
+    par_v = acc_parent[(int64_t)b * T_ + v];
+    x = draft_tok[(int64_t)b * T_ + v];
+    if (verify_row) u = verify_row[(int64_t)b * T_ + v];
+    else if (rule.mode == 0) g_own = argmax[(int64_t)b * T_ + v];
+  }
   // probability rules: every row's log-sum-exp is staged before the same
   // buffer receives the nodes' probabilities
-  if (rule.mode != 0 && v < n) row_lse[v] = rule.prob[(int64_t)b * T_ + v];
+  if (rule.mode != 0 && v < n) sm.row_lse[v] = rule.prob[(int64_t)b * T_ + v];
   __syncthreads();
   if (v < n) {
-    par[v] = acc_parent[(int64_t)b * T_ + v];
+    sm.par[v] = par_v;
     // the row that verifies node v: v itself, or the given row (-1 = accepted
     // unchecked; a row outside [0, n) never accepts)
-    const int u = verify_row ? verify_row[(int64_t)b * T_ + v] : v;
-    const int x = draft_tok[(int64_t)b * T_ + v];
     const bool in_rows = u >= 0 && u < n;
     if (rule.mode == 0) {
-      okv[v] = u == -1 ? 1 : ((in_rows && x == argmax[(int64_t)b * T_ + u]) ? 1 : 0);
+      const int g = verify_row ? (in_rows ? argmax[(int64_t)b * T_ + u] : -1) : g_own;
+      sm.okv[v] = u == -1 ? 1 : ((in_rows && x == g) ? 1 : 0);
     } else {
       // target probability of the draft at its row: exp(logit - lse)
       float p = u == -1 ? 1.f : 0.f;
@@ -332,14 +350,14 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
         const int64_t at = ((int64_t)b * T_ + u) * rule.V + x;
         const float l = rule.logits_bf16 ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(rule.logits)[at]) << 16)
                                          : static_cast<const float*>(rule.logits)[at];
-        p = fast_exp2((l - row_lse[u]) * 1.4426950408889634f);
+        p = fast_exp2((l - sm.row_lse[u]) * 1.4426950408889634f);
       }
       bool ok;
       if (u == -1) ok = true;
       else if (!in_rows) ok = false;
       else if (rule.mode == 1) ok = p > rule.threshold;
       else ok = rule.uniform[(int64_t)b * T_ + v] * rule.draft_prob[(int64_t)b * T_ + v] < p;
-      okv[v] = ok ? 1 : 0;
+      sm.okv[v] = ok ? 1 : 0;
       rule.prob[(int64_t)b * T_ + v] = p;
     }
   }
@@ -348,17 +366,17 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
   // walk to the root; list[] holds the path bottom-up
   int depth = 0;
   bool acc = false;
-  uint8_t* list = lists[v];
+  uint8_t* list = sm.lists[v];
   if (v < n) {
     int cur = v;
     bool good = true;
     while (cur >= 0) {
-      if (depth >= max_depth || !okv[cur]) {
+      if (depth >= max_depth || !sm.okv[cur]) {
         good = false;
         break;
       }
       list[depth++] = (uint8_t)cur;
-      const int p = par[cur];
+      const int p = sm.par[cur];
       if (p < -1 || p >= cur) {   // broken link: not a path to the root
         good = false;
         break;
@@ -372,10 +390,10 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
   int a_len = acc ? depth : 0;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) a_len = max(a_len, __shfl_xor(a_len, o));
-  if (lane == 0) red_i[wave] = a_len;
+  if (lane == 0) sm.red_i[wave] = a_len;
   __syncthreads();
   a_len = 0;
-  for (int w = 0; w < kAccThreads / kWave; ++w) a_len = max(a_len, red_i[w]);
+  for (int w = 0; w < kAccThreads / kWave; ++w) a_len = max(a_len, sm.red_i[w]);
 
   // lexicographically smallest root-first path among accepted nodes of depth A
   uint64_t kh = ~0ull, kl = ~0ull;
@@ -398,22 +416,22 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
     }
   }
   if (lane == 0) {
-    red_h[wave] = kh;
-    red_l[wave] = kl;
+    sm.red_h[wave] = kh;
+    sm.red_l[wave] = kl;
   }
   __syncthreads();
   if (v == 0) {
     for (int w = 1; w < kAccThreads / kWave; ++w)
-      if (key_less(red_h[w], red_l[w], kh, kl)) {
-        kh = red_h[w];
-        kl = red_l[w];
+      if (key_less(sm.red_h[w], sm.red_l[w], kh, kl)) {
+        kh = sm.red_h[w];
+        kl = sm.red_l[w];
       }
     out_len[b] = a_len;
   }
   __syncthreads();
   if (v == 0) {
-    red_h[0] = kh;
-    red_l[0] = kl;
+    sm.red_h[0] = kh;
+    sm.red_l[0] = kl;
     if (out_bonus != nullptr) {
       // correction token: the greedy token of the last accepted node's row
       int bonus = -1;
@@ -430,18 +448,32 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
   if (v < max_depth) {
     int node = -1;
     if (v < a_len) {
-      const uint64_t w = v < 8 ? red_h[0] : red_l[0];
+      const uint64_t w = v < 8 ? sm.red_h[0] : sm.red_l[0];
       const int sh = 56 - 8 * (v & 7);
       node = (int)((w >> sh) & 0xffull);
     }
     out_path[(int64_t)b * max_depth + v] = node;
-    path_s[v] = node;
+    sm.path_s[v] = node;
   }
   // fused form: append the accepted rows to the cache in the same launch
   if (commit.enabled) {
     __syncthreads();
-    commit_rows(b, commit, a_len, path_s);
+    commit_rows(b, commit, a_len, sm.path_s, len_in);
   }
+}
+
+__global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* __restrict__ n_nodes,
+                                                        const int32_t* __restrict__ draft_tok,
+                                                        const int32_t* __restrict__ acc_parent,
+                                                        const int32_t* __restrict__ verify_row,
+                                                        const int32_t* __restrict__ argmax, int max_depth,
+                                                        int32_t* __restrict__ out_len,
+                                                        int32_t* __restrict__ out_path,
+                                                        int32_t* __restrict__ out_bonus, AcceptRule rule,
+                                                        CommitArgs commit) {
+  __shared__ AcceptSmem sm;
+  accept_request(sm, blockIdx.x, T_, n_nodes, draft_tok, acc_parent, verify_row, argmax, max_depth, out_len,
+                 out_path, out_bonus, rule, commit);
 }
 
 hipError_t launch_argmax(const void* logits, int dtype, int B, int T, int V, const int32_t* n_nodes,

@@ -16,8 +16,9 @@ constexpr int kCommitThreads = 256;
 __global__ __launch_bounds__(kCommitThreads) void k_commit(CommitArgs c, const int32_t* __restrict__ out_len,
                                                            const int32_t* __restrict__ out_path, int max_depth) {
   const int b = blockIdx.x;
+  const int64_t len_in = c.cache_len_in[b];
   const int A = clampi(out_len[b], 0, max_depth);
-  commit_rows(b, c, A, out_path + (int64_t)b * max_depth);
+  commit_rows(b, c, A, out_path + (int64_t)b * max_depth, len_in);
 }
 
 hipError_t launch_commit(int B, int Tq, int Hkv, int D, int esize, int64_t lmax, int64_t sb,

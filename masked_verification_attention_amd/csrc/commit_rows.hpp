@@ -10,22 +10,45 @@
 
 namespace sv {
 
-__device__ __forceinline__ void commit_rows(int b, const CommitArgs& c, int A, const int32_t* path) {
-  const int64_t L = min<int64_t>(max(c.cache_len_in[b], 0), c.lmax);
+// len_in is cache_len_in[b], read by the caller as early as it can (it does not
+// depend on the acceptance).  Each thread issues the loads of up to four of its
+// 16-byte chunks before their stores, so the copy costs one memory round trip.
+__device__ __forceinline__ void commit_rows(int b, const CommitArgs& c, int A, const int32_t* path,
+                                            int64_t len_in) {
+  constexpr int kU = 4;
+  const int64_t L = min<int64_t>(max<int64_t>(len_in, 0), c.lmax);
   const int nw = (int)min<int64_t>(A, c.lmax - L);
   const int head_chunks = c.D * c.esize / 16;
   const int row_chunks = c.Hkv * head_chunks;
-  for (int idx = threadIdx.x; idx < nw * row_chunks; idx += blockDim.x) {
-    const int d = idx / row_chunks;
-    const int ch = idx % row_chunks;
-    const int row = path[d];
-    if (row < 0 || row >= c.Tq) continue;
-    const int h = ch / head_chunks;
-    const int cc = ch % head_chunks;
-    const int64_t src = ((((int64_t)b * c.Tq + row) * c.Hkv + h) * c.D) * c.esize + cc * 16;
-    const int64_t dst = ((int64_t)b * c.sb + (L + d) * c.sl + (int64_t)h * c.sh) * c.esize + cc * 16;
-    *reinterpret_cast<u32x4*>(c.k_cache + dst) = ldg16(c.k_blk + src);
-    *reinterpret_cast<u32x4*>(c.v_cache + dst) = ldg16(c.v_blk + src);
+  const int total = nw * row_chunks;
+  for (int i0 = threadIdx.x; i0 < total; i0 += kU * blockDim.x) {
+    u32x4 kx[kU], vx[kU];
+    int64_t dst[kU];
+    bool on[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int idx = i0 + u * blockDim.x;
+      const int d = idx / row_chunks;
+      const int ch = idx % row_chunks;
+      const int row = idx < total ? path[d] : -1;
+      on[u] = row >= 0 && row < c.Tq;
+      dst[u] = 0;
+      if (on[u]) {
+        const int h = ch / head_chunks;
+        const int cc = ch % head_chunks;
+        const int64_t src = ((((int64_t)b * c.Tq + row) * c.Hkv + h) * c.D) * c.esize + cc * 16;
+        dst[u] = ((int64_t)b * c.sb + (L + d) * c.sl + (int64_t)h * c.sh) * c.esize + cc * 16;
+        kx[u] = ldg16(c.k_blk + src);
+        vx[u] = ldg16(c.v_blk + src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (on[u]) {
+        *reinterpret_cast<u32x4*>(c.k_cache + dst[u]) = kx[u];
+        *reinterpret_cast<u32x4*>(c.v_cache + dst[u]) = vx[u];
+      }
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) c.cache_len_out[b] = (int32_t)(L + nw);

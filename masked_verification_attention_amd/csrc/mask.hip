@@ -20,11 +20,14 @@ __global__ __launch_bounds__(kMaskThreads) void k_build_mask(
     const int32_t* __restrict__ n_q, int Tq, int W, uint32_t* __restrict__ mask_bits,
     uint32_t* __restrict__ sp_bits) {
   __shared__ int32_t par[SPEC_MAX_TQ];
+  __shared__ uint8_t spf[SPEC_MAX_TQ];
   __shared__ uint32_t words[SPEC_MAX_TQ][kMaxW + 1];
   const int b = blockIdx.x;
   const int nq = clampi(n_q[b], 0, Tq);
+  // parents and soft-prompt flags in one round trip (coalesced), into LDS
   for (int r = threadIdx.x; r < Tq; r += kMaskThreads) {
     par[r] = attn_parent[(int64_t)b * Tq + r];
+    spf[r] = sp_flag != nullptr ? sp_flag[(int64_t)b * Tq + r] : 0;
     for (int w = 0; w < W; ++w) words[r][w] = 0u;
   }
   __syncthreads();
@@ -45,11 +48,9 @@ __global__ __launch_bounds__(kMaskThreads) void k_build_mask(
   for (int i = threadIdx.x; i < Tq * W; i += kMaskThreads) dst[i] = words[i / W][i % W];
   for (int w = threadIdx.x; w < W; w += kMaskThreads) {
     uint32_t bits = 0u;
-    if (sp_flag != nullptr) {
-      for (int i = 0; i < 32; ++i) {
-        const int r = w * 32 + i;
-        if (r < nq && sp_flag[(int64_t)b * Tq + r] != 0) bits |= 1u << i;
-      }
+    for (int i = 0; i < 32; ++i) {
+      const int r = w * 32 + i;
+      if (r < nq && spf[r] != 0) bits |= 1u << i;
     }
     sp_bits[(int64_t)b * W + w] = bits;
   }

@@ -424,6 +424,12 @@ def test_fused_accept_commit_matches_oracle(name):
                                           x["acc_parent"], st.max_depth)
     np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
     np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
+    greedy = np.argmax(oracle.as_f64(x["logits"], cfg.logits_dtype), axis=-1)
+    got = st.argmax.cpu().numpy()
+    for b in range(x["logits"].shape[0]):
+        n = int(x["n_nodes"][b])
+        np.testing.assert_array_equal(got[b, :n], greedy[b, :n])
+        assert (got[b, n:] == -1).all()
     kc, vc, L2 = oracle.commit_kv(x["k_cache"], x["v_cache"], L0, x["k_blk"], x["v_blk"], A, path)
     np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L2)
     k_host, v_host = st.cache_host()
