@@ -13,8 +13,8 @@ of depth gamma, 1 + sum_{g=1..gamma} k^g nodes, flattened level by level.
 
 Readings taken where the page leaves a step open:
 * "top-k" is the k highest logits of the row, best first, equal logits in
-  increasing token order (k = 1 is the greedy token).  NaN logits are never
-  taken ahead of a number.
+  increasing token order (k = 1 is the greedy token).  NaN logits rank after
+  every number, -inf included, in increasing token order.
 * Within a level, nodes follow their parents' order and, under one parent,
   the rank of their token in the stream's top-k list.
 * The streams' rows are those of the multi-stream layout (``msa.msa_row``) of
@@ -34,8 +34,10 @@ from .msa import msa_row
 def topk_tokens(row: np.ndarray, dtype: str, k: int) -> np.ndarray:
     """The k best token indices of one logit row, best first, ties to the lower index."""
     x = as_f64(np.asarray(row), dtype)
-    key = np.where(np.isnan(x), np.inf, -x)        # NaN after every number
-    order = np.argsort(key, kind="stable")         # stable: equal logits keep index order
+    nan = np.isnan(x)
+    # sort keys, most significant last: numbers before NaN (-inf included), then
+    # larger value first, then lower index first
+    order = np.lexsort((np.arange(x.size), np.where(nan, 0.0, -x), nan))
     return order[:k].astype(np.int32)
 
 

@@ -114,6 +114,34 @@ def test_topk_brute_force_tiny():
         assert tuple(oracle.topk_tokens(row, "f32", k)) == best
 
 
+def test_topk_nan_and_infinities_brute_force():
+    """NaN ranks after every number (-inf included), lowest index first among NaNs;
+    -0 ties with +0.  Checked against the full ordering of every element by
+    (is NaN, larger value first, lower index first), written element by element."""
+    rng = np.random.default_rng(5)
+    choices = np.array([np.nan, -np.inf, np.inf, 0.0, -0.0, 1.0, -1.0], dtype=np.float32)
+    for _ in range(300):
+        V = int(rng.integers(1, 9))
+        k = int(rng.integers(1, V + 1))
+        row = choices[rng.integers(0, len(choices), size=V)]
+
+        def before(a, c):
+            na, nc = bool(np.isnan(row[a])), bool(np.isnan(row[c]))
+            if na != nc:
+                return nc                      # a number before a NaN
+            if not na and row[a] != row[c]:
+                return bool(row[a] > row[c])
+            return a < c
+        order = list(range(V))
+        for i in range(V):                     # selection sort by the rule above
+            m = i
+            for c in range(i + 1, V):
+                if before(order[c], order[m]):
+                    m = c
+            order[i], order[m] = order[m], order[i]
+        assert list(oracle.topk_tokens(row, "f32", k)) == order[:k]
+
+
 def test_next_draft_reads_last_accepted_node_streams():
     # request 0: path 0 -> 2 -> 5, so node 5's stream rows; request 1: nothing accepted;
     # request 2: last node outside the tree
