@@ -106,10 +106,18 @@ def load() -> ctypes.CDLL:
 
 
 def _ptr(x) -> Optional[int]:
+    """Device address of a tensor argument.  The C ABI takes base pointers of
+    dense arrays (the K/V cache's layout goes through the descriptor's strides),
+    so a strided view or a host tensor is refused here rather than handed to a
+    kernel that would read the wrong memory."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError("array arguments must be device (GPU) tensors")
+    if not x.is_contiguous():
+        raise ValueError("array arguments must be contiguous tensors")
     return x.data_ptr()
 
 

@@ -10,14 +10,15 @@
 //
 // k_topk_streams: one workgroup of 1024 threads per (request, stream), two
 // passes over the row with 16-byte loads (eight in flight per thread).  Pass
-// 1 takes each thread's largest value; the k-th largest of those values is a
-// lower bound on the row's k-th best, since it is met by k distinct elements.
-// Pass 2 (the row is then resident in L2) keeps, per thread, a sorted list of
-// the few candidates at or above the bound.  The lists are merged by k rounds
-// of a wave-wide "larger value, then lower index" reduction in which the
-// winning lane pops its list head, first within each wave, then over the
-// waves.  Ties resolve to the lower token index; -0 equals +0; NaN is never
-// preferred to a number.
+// 1 takes each wave's largest value; the k-th largest of the 16 wave maxima
+// is a lower bound on the row's k-th best, since it is met by k distinct
+// elements.  Pass 2 (the row is then resident in L2) keeps, per thread, a
+// sorted list of its best k candidates at or above the bound; the lists are
+// appended to LDS and each entry's rank is the number of entries that rank
+// before it ("larger value, then lower index").  More than 256 entries (long
+// runs of equal values) are merged instead by k rounds of a wave-wide
+// reduction over the lists.  Ties resolve to the lower token index; -0 equals +0; NaN ranks
+// after every number (lowest index first among NaNs).
 //
 // k_draft_tree: one workgroup per request writes tokens and parents.
 #include "device_common.hpp"
@@ -193,13 +194,19 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
     const int32_t* __restrict__ acc_len, const int32_t* __restrict__ acc_path, int max_depth, int gamma,
     int k, int32_t* __restrict__ out_topk) {
   constexpr int K = SPEC_MAX_TOPK;
-  constexpr int U = 8;   // loads in flight per thread
+  constexpr int U = 8;        // loads in flight per thread
+  constexpr int kCap = 256;   // candidates ranked directly; more go through the list merge
   __shared__ float wv[kTopWaves][K];
   __shared__ int wi[kTopWaves][K];
-  __shared__ float bound_v;
+  __shared__ float wmax_s[kTopWaves];
+  __shared__ float cand_v[kCap];
+  __shared__ int cand_i[kCap];
+  __shared__ float bound_s;
+  __shared__ int cnt_s, nan_s;
   const int b = blockIdx.x / gamma;
   const int j = blockIdx.x % gamma;
   const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
   int32_t* dst = out_topk + ((int64_t)b * gamma + j) * k;
   const int row0 = root_stream_row(b, R, gamma, n_nodes, acc_len, acc_path, max_depth);
   if (row0 < 0) {   // uniform over the workgroup
@@ -207,32 +214,90 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
     return;
   }
   const T* base = logits + ((int64_t)b * R + row0 + j) * V;
-  float ov[K];
-  int oi[K];
 
-  // pass 1: each thread's largest value (NaN ignored); the k-th largest of
-  // those values bounds the answer from below
+  // pass 1: the largest value of each wave (NaN ignored).  The k-th largest
+  // of the 16 wave maxima bounds the row's k-th best from below: k distinct
+  // elements reach it.
   float mv = -INFINITY;
   for_row<T, U>(base, V, tid, [&](float x, int) { mv = fmaxf(mv, x); });
-  TopList<K> L;
-  L.clear();
-  L.v[0] = mv;
-  L.i[0] = tid;   // any distinct tag: only the values matter here
-  block_topk<K>(L, k, ov, oi, wv, wi);
-  if (tid == 0) bound_v = ov[k - 1];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mv = fmaxf(mv, __shfl_xor(mv, o));
+  if (lane == 0) wmax_s[wave] = mv;
+  if (tid == 0) cnt_s = 0;
   __syncthreads();
-  const float tv = bound_v;
+  if (tid < kTopWaves) {
+    const float m = wmax_s[tid];
+    int rank = 0;
+    for (int w = 0; w < kTopWaves; ++w) {
+      const float o = wmax_s[w];
+      rank += (o > m || (o == m && w < tid)) ? 1 : 0;
+    }
+    if (rank == k - 1) bound_s = m;
+  }
+  __syncthreads();
+  const float tv = bound_s;
 
-  // pass 2: sorted lists of the candidates (values >= the bound) only
+  // pass 2 (the row is then resident in L2): each thread's sorted list of
+  // its best k candidates, values at or above the bound.  The union of the
+  // lists holds the row's top k (no thread contributes more than k of them),
+  // and every element ranking before one of those is in the union too.  The
+  // lists go to LDS with one append per thread after the pass.
+  TopList<K> L;
   L.clear();
   for_row<T, U>(base, V, tid, [&](float x, int xi) {
     if (x >= tv) L.push(x, xi, k);
   });
-  block_topk<K>(L, k, ov, oi, wv, wi);
-  if (tid == 0) {
+  int mine = 0;
 #pragma unroll
-    for (int r = 0; r < K; ++r)
-      if (r < k) dst[r] = oi[r] == 0x7fffffff ? -1 : oi[r];
+  for (int q = 0; q < K; ++q) mine += (q < k && L.i[q] != 0x7fffffff) ? 1 : 0;
+  if (mine > 0) {
+    const int at = atomicAdd(&cnt_s, mine);
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      if (q < mine && at + q < kCap) {
+        cand_v[at + q] = L.v[q];
+        cand_i[at + q] = L.i[q];
+      }
+    }
+  }
+  __syncthreads();
+  const int n = cnt_s;
+  if (n <= kCap) {
+    // each candidate's rank is the number of candidates ranking before it
+    if (tid < n) {
+      const float cv = cand_v[tid];
+      const int ci = cand_i[tid];
+      int rank = 0;
+      for (int c = 0; c < n; ++c) rank += ranks_before(cand_v[c], cand_i[c], cv, ci) ? 1 : 0;
+      if (rank < k) dst[rank] = ci;
+    }
+    // Fewer than k numbers in the row (the bound is then -inf and every
+    // number is a candidate): NaN entries follow every number, lowest index
+    // first, one block-wide minimum per missing place.
+    int prev = -1;
+    for (int r = n; r < k; ++r) {
+      if (tid == 0) nan_s = 0x7fffffff;
+      __syncthreads();
+      int mine = 0x7fffffff;
+      for_row<T, U>(base, V, tid, [&](float x, int xi) {
+        if (x != x && xi > prev && xi < mine) mine = xi;
+      });
+      if (mine != 0x7fffffff) atomicMin(&nan_s, mine);
+      __syncthreads();
+      const int got = nan_s;
+      __syncthreads();
+      if (tid == 0) dst[r] = got == 0x7fffffff ? -1 : got;
+      prev = got;
+    }
+  } else {
+    float ov[K];
+    int oi[K];
+    block_topk<K>(L, k, ov, oi, wv, wi);
+    if (tid == 0) {
+#pragma unroll
+      for (int r = 0; r < K; ++r)
+        if (r < k) dst[r] = oi[r] == 0x7fffffff ? -1 : oi[r];
+    }
   }
 }
 

@@ -214,3 +214,12 @@ def test_workspace_policy():
     la32 = good_desc(B=8, Tq=8, Hq=32, Hkv=32, S=0, lmax=2056, dtype=bd.SPEC_F32,
                      strides=(2056 * 32 * 128, 32 * 128, 128))
     assert bd.spec_verify_attn_workspace(la32) > 0
+
+
+def test_binding_refuses_host_tensors():
+    # a host tensor's address must never reach a kernel: the binding refuses it
+    # before calling into the library
+    import torch
+    host = torch.zeros(2, 8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device"):
+        bd.spec_build_mask(host, None, FAKE, 2, 8, FAKE, FAKE, stream=0)
