@@ -129,12 +129,16 @@ __device__ __forceinline__ int row_argmax(const T* __restrict__ base, int V, flo
   int bi = bi0;
   better(bv, bi, bv1, bi1);
 
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(bv, o);
-    const int oi = __shfl_xor(bi, o);
-    better(bv, bi, ov, oi);
-  }
+  uint32_t pair[2] = {__float_as_uint(bv), (uint32_t)bi};
+  wave_allreduce<2>(pair, [](uint32_t (&x)[2], const uint32_t (&y)[2]) {
+    float v = __uint_as_float(x[0]);
+    int i = (int)x[1];
+    better(v, i, __uint_as_float(y[0]), (int)y[1]);
+    x[0] = __float_as_uint(v);
+    x[1] = (uint32_t)i;
+  });
+  bv = __uint_as_float(pair[0]);
+  bi = (int)pair[1];
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x % kWave) == 0) {
     sv_[wave] = bv;
@@ -387,9 +391,9 @@ __device__ __forceinline__ void accept_request(AcceptSmem& sm, int b, int T_, co
   }
 
   // A = deepest accepted node
-  int a_len = acc ? depth : 0;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) a_len = max(a_len, __shfl_xor(a_len, o));
+  uint32_t alw[1] = {(uint32_t)(acc ? depth : 0)};
+  wave_allreduce<1>(alw, [](uint32_t (&x)[1], const uint32_t (&y)[1]) { x[0] = max(x[0], y[0]); });
+  int a_len = (int)alw[0];
   if (lane == 0) sm.red_i[wave] = a_len;
   __syncthreads();
   a_len = 0;
@@ -406,15 +410,17 @@ __device__ __forceinline__ void accept_request(AcceptSmem& sm, int b, int T_, co
       else kl |= node << (56 - 8 * (d - 8));
     }
   }
+  uint32_t kw[4] = {(uint32_t)kh, (uint32_t)(kh >> 32), (uint32_t)kl, (uint32_t)(kl >> 32)};
+  wave_allreduce<4>(kw, [](uint32_t (&x)[4], const uint32_t (&y)[4]) {
+    const uint64_t xh = x[0] | ((uint64_t)x[1] << 32), xl = x[2] | ((uint64_t)x[3] << 32);
+    const uint64_t yh = y[0] | ((uint64_t)y[1] << 32), yl = y[2] | ((uint64_t)y[3] << 32);
+    if (key_less(yh, yl, xh, xl)) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t oh = __shfl_xor(kh, o);
-    const uint64_t ol = __shfl_xor(kl, o);
-    if (key_less(oh, ol, kh, kl)) {
-      kh = oh;
-      kl = ol;
+      for (int q = 0; q < 4; ++q) x[q] = y[q];
     }
-  }
+  });
+  kh = kw[0] | ((uint64_t)kw[1] << 32);
+  kl = kw[2] | ((uint64_t)kw[3] << 32);
   if (lane == 0) {
     sm.red_h[wave] = kh;
     sm.red_l[wave] = kl;

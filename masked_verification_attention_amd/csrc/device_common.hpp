@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sv {
 
 constexpr int kWave = 64;
@@ -41,6 +43,48 @@ __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
+}
+
+// Cross-lane moves by DPP, a modifier of a plain vector move (no LDS round
+// trip, unlike __shfl_xor, which becomes ds_bpermute).  Within each row of 16
+// lanes: 0xB1 swaps neighbours (lane ^ 1), 0x4E swaps pairs (lane ^ 2), 0x141
+// mirrors each half-row (lane i <-> 7 - i), 0x140 mirrors the row
+// (i <-> 15 - i).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+// All-reduce of an N-word state over the 64 lanes of a wave, every lane
+// active: four DPP stages make each row of 16 lanes agree (swap neighbours,
+// swap pairs, then mirror halves and rows, so every stage folds two disjoint
+// groups), then the four row results are read into scalars and folded.
+// combine(a, b) folds b into a and must be associative and commutative (a
+// selection by a total order is).  Every lane gets the result.
+template <int N, typename Combine>
+__device__ __forceinline__ void wave_allreduce(uint32_t (&w)[N], Combine combine) {
+  auto stage = [&](auto ctrl) __attribute__((always_inline)) {
+    uint32_t o[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) o[q] = dpp_u32<decltype(ctrl)::value>(w[q]);
+    combine(w, o);
+  };
+  stage(std::integral_constant<int, 0xB1>{});
+  stage(std::integral_constant<int, 0x4E>{});
+  stage(std::integral_constant<int, 0x141>{});
+  stage(std::integral_constant<int, 0x140>{});
+  uint32_t r[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) r[q] = (uint32_t)__builtin_amdgcn_readlane((int)w[q], 0);
+#pragma unroll
+  for (int row = 1; row < 4; ++row) {
+    uint32_t o[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) o[q] = (uint32_t)__builtin_amdgcn_readlane((int)w[q], 16 * row);
+    combine(r, o);
+  }
+#pragma unroll
+  for (int q = 0; q < N; ++q) w[q] = r[q];
 }
 
 // 16-byte global load through the vector path.

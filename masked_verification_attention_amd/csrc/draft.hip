@@ -220,8 +220,11 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
   // elements reach it.
   float mv = -INFINITY;
   for_row<T, U>(base, V, tid, [&](float x, int) { mv = fmaxf(mv, x); });
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mv = fmaxf(mv, __shfl_xor(mv, o));
+  uint32_t mw[1] = {__float_as_uint(mv)};
+  wave_allreduce<1>(mw, [](uint32_t (&x)[1], const uint32_t (&y)[1]) {
+    x[0] = __float_as_uint(fmaxf(__uint_as_float(x[0]), __uint_as_float(y[0])));
+  });
+  mv = __uint_as_float(mw[0]);
   if (lane == 0) wmax_s[wave] = mv;
   if (tid == 0) cnt_s = 0;
   __syncthreads();
