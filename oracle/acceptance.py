@@ -6,7 +6,9 @@ Definitions:
   row (hard matching in the verification step of Speculative Streaming; the
   check of predictions at the lookahead positions in Lookahead Attention
   section 2.3).  Row v verifies node v.  Ties go to the lowest index, and
-  -0 equals +0 (``numpy.argmax`` returns the first maximal entry).
+  -0 equals +0.  NaN logits rank after every number (-inf included), so a
+  row's greedy token is a NaN entry only when the row holds no number (then
+  its first entry); this is the top-1 of the tree draft's top-k rule.
 * Node v matches when its drafted token equals its greedy target token.  It
   is accepted when it matches and so does every node on its path from the
   root (a branch is followed until a rejection).  Its depth is the number of
@@ -31,8 +33,15 @@ from .bf16 import as_f64
 
 
 def greedy_tokens(logits: np.ndarray, logits_dtype: str) -> np.ndarray:
-    """Per-row argmax over the vocabulary (first maximal index). [B, T] int32."""
-    return np.argmax(as_f64(logits, logits_dtype), axis=-1).astype(np.int32)
+    """Per-row argmax over the vocabulary: the first index of the largest
+    number, NaN ignored; a row of NaN only gives 0.  [..., V] -> [...] int32."""
+    x = as_f64(logits, logits_dtype)
+    nan = np.isnan(x)
+    num = np.where(nan, -np.inf, x)
+    top = num.max(axis=-1, keepdims=True)
+    is_top = (num == top) & ~nan                      # numbers equal to the row's largest
+    first_top = np.argmax(is_top, axis=-1)            # first True
+    return np.where(is_top.any(axis=-1), first_top, 0).astype(np.int32)
 
 
 def accept_request(draft_tok, acc_parent, greedy, n_nodes: int, max_depth: int):

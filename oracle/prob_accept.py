@@ -29,6 +29,7 @@ the soft rule's product u * p_d is a float32 product.
 
 import numpy as np
 
+from .acceptance import greedy_tokens
 from .bf16 import as_f64
 
 MODE_THRESHOLD = 1
@@ -107,7 +108,7 @@ def prob_accept(logits, logits_dtype: str, n_nodes, draft_tok, acc_parent, verif
     """Batch form: (greedy [B, T], p [B, T], ok [B, T], out_len [B], out_path [B, max_depth],
     out_bonus [B]).  ``p`` overrides the target probabilities (to replay a given set)."""
     B, T, V = logits.shape
-    greedy = np.argmax(as_f64(logits, logits_dtype), axis=-1).astype(np.int32)
+    greedy = greedy_tokens(logits, logits_dtype)
     if p is None:
         p = node_probs(logits, logits_dtype, n_nodes, draft_tok, verify_row)
     ok = np.zeros((B, T), dtype=bool)

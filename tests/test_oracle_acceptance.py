@@ -38,6 +38,31 @@ def test_argmax_first_max_on_ties_and_signed_zero():
     assert list(oracle.greedy_tokens(bits[None], "bf16")[0]) == [0, 0, 1, 1, 0]
 
 
+def test_argmax_with_nan_and_infinities_is_the_top1_rule():
+    """NaN ranks after every number, -inf included: the greedy token equals the
+    first entry of the tree draft's top-k order, checked element by element
+    against a loop that skips NaN and takes a NaN only for a row of NaN."""
+    rng = np.random.default_rng(9)
+    choices = np.array([np.nan, -np.inf, np.inf, 0.0, -0.0, 1.0, -1.0], dtype=np.float32)
+
+    def loop(row):
+        best, idx = None, -1
+        for i, x in enumerate(row):
+            if np.isnan(x):
+                continue
+            if best is None or x > best:
+                best, idx = x, i
+        return 0 if idx < 0 else idx
+
+    rows = choices[rng.integers(0, len(choices), size=(400, 7))]
+    rows[0] = np.nan                       # no number at all
+    rows[1] = [np.nan, -np.inf, np.nan, -np.inf, np.nan, np.nan, np.nan]
+    got = oracle.greedy_tokens(rows[None], "f32")[0]
+    assert list(got) == [loop(r) for r in rows]
+    assert got[0] == 0 and got[1] == 1
+    assert all(g == oracle.topk_tokens(r, "f32", 1)[0] for g, r in zip(got, rows))
+
+
 def test_argmax_random_bf16_rows_with_natural_ties():
     rng = np.random.Generator(np.random.PCG64(3))
     x = wl.f32_to_bf16_bits(rng.standard_normal((64, 32000), dtype=np.float32))
