@@ -80,10 +80,32 @@ __device__ __forceinline__ void scan16(float& bv, int& bi, const u32x4& x, int i
   }
 }
 
-// First maximum of one logit row by the whole workgroup; the index is valid
-// in thread 0.
+// First entry of a row that is a number, or 0 for a row of NaN only: the
+// greedy token of a row none of whose entries exceeds -inf.  One more pass by
+// the whole workgroup (rows like this do not occur in practice); s_min is an
+// LDS word.
 template <typename T>
-__device__ __forceinline__ int row_argmax(const T* __restrict__ base, int V, float* sv_, int* si_) {
+__device__ __noinline__ int first_number(const T* __restrict__ base, int V, int* s_min) {
+  if (threadIdx.x == 0) *s_min = 0x7fffffff;
+  __syncthreads();
+  int mine = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += kArgThreads) {
+    const float x = elem_at<T>(base, i);
+    if (x == x) {
+      mine = i;
+      break;
+    }
+  }
+  if (mine != 0x7fffffff) atomicMin(s_min, mine);
+  __syncthreads();
+  const int r = *s_min;
+  return r == 0x7fffffff ? 0 : r;
+}
+
+// First maximum of one logit row by the whole workgroup (NaN ranks after every
+// number); every thread gets the index.  res is an LDS word.
+template <typename T>
+__device__ __forceinline__ int row_argmax(const T* __restrict__ base, int V, float* sv_, int* si_, int* res) {
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
   constexpr int U = 8;               // 16-byte loads in flight per thread
   const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
@@ -147,9 +169,13 @@ __device__ __forceinline__ int row_argmax(const T* __restrict__ base, int V, flo
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kArgThreads / kWave; ++w) better(bv, bi, sv_[w], si_[w]);
+    *res = bi;
   }
-  // a row of -inf only: every element ties, the first index wins
-  return bi == 0x7fffffff ? 0 : bi;
+  __syncthreads();
+  // the scan only takes values above -inf: a row without one gets its first
+  // number (a -inf) or 0 in a second pass
+  const int top = *res;
+  return top == 0x7fffffff ? first_number<T>(base, V, si_) : top;
 }
 
 template <typename T>
@@ -158,6 +184,7 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ lo
                                                         int32_t* __restrict__ out) {
   __shared__ float sv_[kArgThreads / kWave];
   __shared__ int si_[kArgThreads / kWave];
+  __shared__ int res;
   const int row = blockIdx.x;
   const int b = row / T_;
   const int v = row % T_;
@@ -166,14 +193,15 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ lo
     if (threadIdx.x == 0) out[row] = -1;
     return;
   }
-  const int bi = row_argmax<T>(logits + (int64_t)row * V, V, sv_, si_);
+  const int bi = row_argmax<T>(logits + (int64_t)row * V, V, sv_, si_, &res);
   if (threadIdx.x == 0) out[row] = bi;
 }
 
 // k_argmax_lse: the greedy token and the log-sum-exp of every node row, for
 // acceptance by probability.  Same stream as k_argmax; each thread also keeps
 // a running maximum m and sum s of exp(x - m) (in the log2 domain), moving m
-// once per 16-byte vector; the workgroup merges (m, s) pairs.  Rows past
+// once per 16-byte vector; the workgroup merges (m, s) pairs.  A row holding a
+// NaN entry gets a NaN log-sum-exp (its softmax is undefined), and rows past
 // n_nodes get argmax -1 and a NaN log-sum-exp.
 template <typename T>
 __global__ __launch_bounds__(kArgThreads) void k_argmax_lse(const T* __restrict__ logits, int T_, int V,
@@ -186,6 +214,7 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax_lse(const T* __restrict_
   __shared__ int si_[kArgThreads / kWave];
   __shared__ float sm_[kArgThreads / kWave];
   __shared__ float ss_[kArgThreads / kWave];
+  __shared__ int sn_[kArgThreads / kWave];
   const int row = blockIdx.x;
   const int b = row / T_;
   const int v = row % T_;
@@ -200,7 +229,9 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax_lse(const T* __restrict_
   const T* base = logits + (int64_t)row * V;
   float bv = -INFINITY, m = -INFINITY, s = 0.f;   // m, s in log2 units
   int bi = 0x7fffffff;
+  bool nanf = false;                                // a NaN entry makes the row's log-sum-exp NaN
   auto add = [&](float x, int i) {
+    nanf = nanf || x != x;
     better(bv, bi, x, i);
     const float y = x * kLog2e;
     if (y > m) {
@@ -214,6 +245,24 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax_lse(const T* __restrict_
   for (int i = threadIdx.x; i < pre; i += kArgThreads) add(elem_at<T>(base, i), i);
   const int nvec = (V - pre) / E;
   const char* vb = reinterpret_cast<const char*>(base + pre);
+  auto unpack = [&](const u32x4& x, float (&xs)[E]) __attribute__((always_inline)) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xs[2 * e] = bf16lo(w[e]);
+        xs[2 * e + 1] = bf16hi(w[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[e] = __uint_as_float(w[e]);
+    }
+  };
+  // Vectors: the largest number of each (NaN ignored) and the first vector
+  // holding the thread's largest; the entry's index is recovered after the
+  // scan from that one vector.
+  float vv = -INFINITY;
+  int vc = -1;
   constexpr int RV = U * kArgThreads;
   for (int r0 = 0; r0 < nvec; r0 += RV) {
     u32x4 x[U];
@@ -226,41 +275,41 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax_lse(const T* __restrict_
     for (int u = 0; u < U; ++u) {
       const int c = r0 + u * kArgThreads + (int)threadIdx.x;
       if (c >= nvec) continue;
-      const int i0 = pre + c * E;
       float xs[E];
-      const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xs[2 * e] = bf16lo(w[e]);
-          xs[2 * e + 1] = bf16hi(w[e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xs[e] = __uint_as_float(w[e]);
-      }
-      // indices increase within the vector: a strict ">" keeps the first maximum
+      unpack(x[u], xs);
       float cm = xs[0];
-      int ci = i0;
 #pragma unroll
-      for (int e = 1; e < E; ++e)
-        if (xs[e] > cm) {
-          cm = xs[e];
-          ci = i0 + e;
-        }
-      better(bv, bi, cm, ci);
+      for (int e = 1; e < E; ++e) cm = fmaxf(cm, xs[e]);
+      // a strict ">" keeps the first vector; the first vector holding a number
+      // is taken even when that number is -inf
+      const bool up = cm > vv || (vc < 0 && cm == cm);
+      vv = up ? cm : vv;
+      vc = up ? c : vc;
       const float ym = cm * kLog2e;
       if (ym > m) {
         s = m == -INFINITY ? 0.f : s * fast_exp2(m - ym);
         m = ym;
       }
       if (m != -INFINITY) {
+        // a NaN entry turns s into NaN here
 #pragma unroll
         for (int e = 0; e < E; ++e) s += fast_exp2(xs[e] * kLog2e - m);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) nanf = nanf || xs[e] != xs[e];
       }
     }
   }
+  if (vc >= 0) {
+    float xs[E];
+    unpack(ldg16(vb + (int64_t)vc * 16), xs);
+    int vi = pre + vc * E;
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e) vi = xs[e] == vv ? pre + vc * E + e : vi;
+    better(bv, bi, vv, vi);
+  }
   for (int i = pre + nvec * E + threadIdx.x; i < V; i += kArgThreads) add(elem_at<T>(base, i), i);
+  nanf = __any(nanf);
 
   auto merge = [&](float om, float os) {
     const float M = fmaxf(m, om);
@@ -283,15 +332,18 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax_lse(const T* __restrict_
     si_[wave] = bi;
     sm_[wave] = m;
     ss_[wave] = s;
+    sn_[wave] = nanf ? 1 : 0;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kArgThreads / kWave; ++w) {
       better(bv, bi, sv_[w], si_[w]);
       merge(sm_[w], ss_[w]);
+      nanf = nanf || sn_[w] != 0;
     }
+    // a row of NaN only: its first entry
     out[row] = bi == 0x7fffffff ? 0 : bi;
-    lse[row] = (m + fast_log2(s)) * 0.69314718055994531f;
+    lse[row] = nanf ? __builtin_nanf("") : (m + fast_log2(s)) * 0.69314718055994531f;
   }
 }
 

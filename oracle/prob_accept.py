@@ -39,9 +39,10 @@ MODE_SOFT = 2
 def target_prob(row: np.ndarray, dtype: str, x: int) -> float:
     """softmax(row)[x] in float64."""
     z = as_f64(np.asarray(row), dtype)
-    m = z.max()
-    e = np.exp(z - m)
-    return float(e[x] / e.sum())
+    with np.errstate(invalid="ignore", over="ignore"):   # NaN / infinite rows give NaN, as intended
+        m = z.max()
+        e = np.exp(z - m)
+        return float(e[x] / e.sum())
 
 
 def node_probs(logits, dtype: str, n_nodes, draft_tok, verify_row):

@@ -199,3 +199,72 @@ def test_step_with_probability_acceptance(rule):
     np.testing.assert_array_equal(k_host, kc)
     np.testing.assert_array_equal(v_host, vc)
     say(f"    {rule}: accepted {A.tolist()}")
+
+
+def _edge_rows(V, rng):
+    """Rows for the NaN and infinity rules: NaN as the first entry of many 16-byte
+    vectors, a row whose only numbers are -inf, a row of NaN only, a row of -inf
+    only, +inf entries, ties across vectors, signed zeros."""
+    rows = []
+    a = rng.standard_normal(V).astype(np.float32)
+    a[::8] = np.nan                                  # first entry of every bf16 vector
+    a[::4] = np.where(np.arange(0, V, 4) % 8 == 0, np.nan, a[::4])
+    rows.append(a)
+    a = np.full(V, np.nan, np.float32)
+    a[[7, 300]] = -np.inf
+    rows.append(a)
+    rows.append(np.full(V, np.nan, np.float32))
+    rows.append(np.full(V, -np.inf, np.float32))
+    a = rng.standard_normal(V).astype(np.float32)
+    a[[1000, 17]] = np.inf
+    rows.append(a)
+    a = rng.standard_normal(V).astype(np.float32)
+    a[rng.choice(V, 40, replace=False)] = a.max() + 1.0
+    rows.append(a)
+    a = np.where(rng.random(V) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    rows.append(a)
+    rows.append(rng.standard_normal(V).astype(np.float32))
+    return np.stack(rows)
+
+
+def _bits(a):
+    bits = wl.f32_to_bf16_bits(np.nan_to_num(a, nan=0.0, posinf=0.0, neginf=0.0))
+    bits = np.where(np.isnan(a), np.uint16(0x7fc0), bits)
+    bits = np.where(np.isposinf(a), np.uint16(0x7f80), bits)
+    bits = np.where(np.isneginf(a), np.uint16(0xff80), bits)
+    return bits.astype(np.uint16)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_greedy_token_and_probabilities_with_nan_and_infinities(dt):
+    """Both argmax kernels follow the greedy rule on crafted rows (NaN after every
+    number, first index on ties); the probability is NaN exactly where the
+    oracle's is (a NaN entry, or a row without a finite maximum)."""
+    rng = np.random.default_rng(23)
+    V = 5003                                         # odd: rows start misaligned
+    rows = _edge_rows(V, rng)
+    T = rows.shape[0]
+    raw = np.ascontiguousarray(rows[None], dtype=np.float32)       # B = 1
+    data = _bits(raw) if dt == "bf16" else raw
+    want = oracle.greedy_tokens(data, dt)
+    n_nodes = np.array([T], dtype=np.int32)
+    parent = np.arange(-1, T - 1, dtype=np.int32)[None]
+    draft = want.copy().astype(np.int32)
+    draft[0, 3] = 5                                  # a draft the -inf row's token is not
+    say(f"[gpu] argmax / lse edge rows {dt}: V={V} rows={T}")
+    # the greedy kernel (spec_argmax_accept)
+    dev = dict(dtype=torch.int32, device="cuda")
+    am = torch.full((1, T), -9, **dev)
+    ln = torch.full((1,), -9, **dev)
+    pth = torch.full((1, 8), -9, **dev)
+    bd.spec_argmax_accept(upload(data, dt), bd.SPEC_BF16 if dt == "bf16" else bd.SPEC_F32, 1, T, V,
+                          upload(n_nodes), upload(draft), upload(parent), 8, am, ln, pth)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(am.cpu().numpy(), want)
+    # the greedy token + log-sum-exp kernel (spec_prob_accept)
+    got_am, prob, _, _, _ = run(data, dt, n_nodes, draft, parent, None, 8, bd.SPEC_ACCEPT_THRESHOLD, 0.5)
+    np.testing.assert_array_equal(got_am, want)
+    ref_p = oracle.node_probs(data, dt, n_nodes, draft, None)
+    np.testing.assert_array_equal(np.isnan(prob), np.isnan(ref_p))
+    fin = ~np.isnan(ref_p)
+    np.testing.assert_allclose(prob[fin], ref_p[fin], rtol=P_RTOL, atol=0)
