@@ -1,0 +1,61 @@
+"""The verification step captured in a HIP graph (torch's CUDAGraph around the
+library's launches): the library allocates nothing and clears nothing with
+memsets on this path, so every replay must reproduce the eager results.  Each
+replay is checked, with eager work and synchronisation between replays."""
+
+import sys
+
+import pytest
+import torch
+
+from masked_verification_attention_amd import workloads as wl
+from masked_verification_attention_amd.step import VerifyStep
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("name", ["c3_confu_8b", "c6_msa_1b"])
+def test_graph_replays_match_eager(name):
+    cfg = wl.CONFIGS[name]
+    sts = [VerifyStep(cfg, wl.generate(cfg, B=2, seed=cfg.seed + 7 * j), layout="bhld") for j in range(2)]
+    for s in sts:
+        s.run()
+    torch.cuda.synchronize()
+
+    def outputs(s):
+        outs = [s.out, s.lse, s.argmax, s.out_len, s.out_path, s.cache_len_out]
+        if s.msa:
+            outs += [s.out_bonus, s.next_tok, s.next_parent, s.next_n]
+        return outs
+
+    ref = [[t.clone() for t in outputs(s)] for s in sts]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in sts:
+            s.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for s in sts:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s.run()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    say(f"[gpu] graph {name}: captured {len(graphs)} steps")
+    for rep in range(3):
+        for i, (s, g) in enumerate(zip(sts, graphs)):
+            for t in outputs(s):
+                t.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(outputs(s), ref[i]):
+                assert torch.equal(a, b), (rep, i)
+            s.run()                                   # eager work between replays
+            torch.cuda.synchronize()
