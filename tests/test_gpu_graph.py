@@ -59,3 +59,29 @@ def test_graph_replays_match_eager(name):
                 assert torch.equal(a, b), (rep, i)
             s.run()                                   # eager work between replays
             torch.cuda.synchronize()
+
+
+def test_concurrent_streams_match_serial():
+    """Two independent steps launched on two streams at once (the library keeps
+    no state between calls) give the results they give one after the other."""
+    cfg = wl.CONFIGS["c3_confu_8b"]
+    sts = [VerifyStep(cfg, wl.generate(cfg, B=3, seed=cfg.seed + 11 * j), layout="bhld") for j in range(2)]
+    for s in sts:
+        s.run()
+    torch.cuda.synchronize()
+    ref = [[t.clone() for t in (s.out, s.lse, s.argmax, s.out_len, s.out_path, s.cache_len_out)] for s in sts]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(5):
+        for s in sts:
+            for t in (s.out, s.lse, s.argmax, s.out_len, s.out_path, s.cache_len_out):
+                t.fill_(-7)
+        torch.cuda.synchronize()
+        for s, st in zip(sts, streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                s.run()
+        torch.cuda.synchronize()
+        for s, r in zip(sts, ref):
+            for a, b in zip((s.out, s.lse, s.argmax, s.out_len, s.out_path, s.cache_len_out), r):
+                assert torch.equal(a, b), rep
+    say("[gpu] two streams: 5 concurrent rounds match the serial results")
