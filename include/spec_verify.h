@@ -208,7 +208,9 @@ int spec_build_msa_mask(const int32_t* tree_parent, const int32_t* n_nodes, int3
  *   out_prob    [B, T] float out: p of each node (1 for the unchecked root, 0
  *               for a row or token out of range; NaN past n_nodes[b]).
  *
- * Limits as spec_argmax_accept_rows; logits must be finite.
+ * Limits as spec_argmax_accept_rows.  A row holding a NaN logit, or none
+ * above -inf, has an undefined softmax: its p is NaN and its drafts are not
+ * accepted.
  */
 int spec_prob_accept(const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,
                      const int32_t* n_nodes, const int32_t* draft_tok, const int32_t* acc_parent,
@@ -234,7 +236,8 @@ int spec_prob_accept(const void* logits, int32_t logits_dtype, int32_t B, int32_
  * spec_build_msa_mask directly.
  *
  *   logits      [B, R, V] float32 or bf16 (logits_dtype), the block's rows;
- *               finite, or NaN, which is never preferred to a number.
+ *               NaN ranks after every number (-inf included), NaN entries
+ *               in increasing token order.
  *   n_nodes     [B] int32   nodes of the verified tree.
  *   acc_len     [B] int32, acc_path [B, max_depth] int32: the accepted paths
  *               (spec_argmax_accept_rows' out_len and out_path).
@@ -308,7 +311,8 @@ int spec_verify_attn(const spec_attn_desc* d, const void* q,
  *
  * For node v < n_nodes[b] ([SS] verification step, hard matching; [LA] 2.3):
  *   out_argmax[b][v] = index of the largest logits[b][v][:] (lowest index
- *                      on ties; -0 == +0; logits must not be NaN)
+ *                      on ties; -0 == +0; NaN ranks after every number,
+ *                      so a row of NaN only gives 0)
  *   match(v)  = draft_tok[b][v] == out_argmax[b][v]
  *   accepted(v) = match(v) and (acc_parent[b][v] == -1 or accepted(parent)),
  *                 and depth(v) <= max_depth (depth 1 for parent -1)
