@@ -104,10 +104,9 @@ __device__ __noinline__ int first_number(const T* __restrict__ base, int V, int*
 
 // First maximum of one logit row by the whole workgroup (NaN ranks after every
 // number); every thread gets the index.  res is an LDS word.
-template <typename T>
+template <typename T, int U>   // U: 16-byte loads in flight per thread and buffer
 __device__ __forceinline__ int row_argmax(const T* __restrict__ base, int V, float* sv_, int* si_, int* res) {
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
-  constexpr int U = 8;               // 16-byte loads in flight per thread
   const int mis = (int)(((uintptr_t)base & 15u) / sizeof(T));
   const int pre = min(V, mis == 0 ? 0 : E - mis);
   // two independent running maxima (even / odd load slots) shorten the dependency chain
@@ -178,7 +177,7 @@ __device__ __forceinline__ int row_argmax(const T* __restrict__ base, int V, flo
   return top == 0x7fffffff ? first_number<T>(base, V, si_) : top;
 }
 
-template <typename T>
+template <typename T, int U>
 __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ logits, int T_, int V,
                                                         const int32_t* __restrict__ n_nodes,
                                                         int32_t* __restrict__ out) {
@@ -193,7 +192,7 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax(const T* __restrict__ lo
     if (threadIdx.x == 0) out[row] = -1;
     return;
   }
-  const int bi = row_argmax<T>(logits + (int64_t)row * V, V, sv_, si_, &res);
+  const int bi = row_argmax<T, U>(logits + (int64_t)row * V, V, sv_, si_, &res);
   if (threadIdx.x == 0) out[row] = bi;
 }
 
@@ -537,12 +536,23 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(int T_, const int32_t* _
 hipError_t launch_argmax(const void* logits, int dtype, int B, int T, int V, const int32_t* n_nodes,
                          int32_t* out_argmax, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)B * T));
-  if (dtype == SPEC_F32)
-    hipLaunchKernelGGL(k_argmax<float>, grid, dim3(kArgThreads), 0, st, static_cast<const float*>(logits), T,
-                       V, n_nodes, out_argmax);
-  else
-    hipLaunchKernelGGL(k_argmax<uint16_t>, grid, dim3(kArgThreads), 0, st,
-                       static_cast<const uint16_t*>(logits), T, V, n_nodes, out_argmax);
+  // Rows of at most 128 KB are latency-bound (a workgroup streams one row):
+  // 16 loads in flight per thread bring them in about one round trip.  Longer
+  // rows are bandwidth-bound, where 8 measured faster.
+  const bool short_row = (int64_t)V * (dtype == SPEC_F32 ? 4 : 2) <= (128 << 10);
+  if (dtype == SPEC_F32) {
+    const float* lg = static_cast<const float*>(logits);
+    if (short_row)
+      hipLaunchKernelGGL((k_argmax<float, 16>), grid, dim3(kArgThreads), 0, st, lg, T, V, n_nodes, out_argmax);
+    else
+      hipLaunchKernelGGL((k_argmax<float, 8>), grid, dim3(kArgThreads), 0, st, lg, T, V, n_nodes, out_argmax);
+  } else {
+    const uint16_t* lg = static_cast<const uint16_t*>(logits);
+    if (short_row)
+      hipLaunchKernelGGL((k_argmax<uint16_t, 16>), grid, dim3(kArgThreads), 0, st, lg, T, V, n_nodes, out_argmax);
+    else
+      hipLaunchKernelGGL((k_argmax<uint16_t, 8>), grid, dim3(kArgThreads), 0, st, lg, T, V, n_nodes, out_argmax);
+  }
   return hipGetLastError();
 }
 
