@@ -22,9 +22,9 @@ nodes never accepts, and the correction token is the greedy token of the last
 accepted node's row (this reading keeps the correction deterministic; the
 pages' residual resampling needs the draft's whole distribution).
 
-Where the decision is a floating-point comparison it is taken in float32, the
-kernel's precision: the float64 probability is rounded to float32 first, and
-the soft rule's product u * p_d is a float32 product.
+Both decisions are the real-valued comparisons the pages state, taken in
+float64: p_t is the float64 softmax, and the inputs threshold, u and p_d are
+widened exactly (they arrive as float32 or Python floats).
 """
 
 import numpy as np
@@ -65,12 +65,14 @@ def node_probs(logits, dtype: str, n_nodes, draft_tok, verify_row):
 
 
 def decide(p: float, mode: int, threshold: float = 0.0, draft_p: float = 1.0, u: float = 0.0) -> bool:
-    """One node's acceptance from its target probability, decided in float32."""
-    p32 = np.float32(p)
+    """One node's acceptance from its target probability p (float64): the threshold
+    rule p > threshold, or soft matching u < min(1, p / p_d), written u * p_d < p so
+    that p_d = 0 needs no division (a NaN p accepts under neither rule)."""
+    p = float(p)
     if mode == MODE_THRESHOLD:
-        return bool(p32 > np.float32(threshold))
+        return p > float(threshold)
     if mode == MODE_SOFT:
-        return bool(np.float32(np.float32(u) * np.float32(draft_p)) < p32)
+        return float(u) * float(draft_p) < p
     raise ValueError(mode)
 
 
@@ -105,13 +107,12 @@ def scan_accepted(ok, acc_parent, n: int, max_depth: int):
 
 
 def prob_accept(logits, logits_dtype: str, n_nodes, draft_tok, acc_parent, verify_row, max_depth: int,
-                mode: int, threshold: float = 0.0, draft_prob=None, uniform=None, p=None):
+                mode: int, threshold: float = 0.0, draft_prob=None, uniform=None):
     """Batch form: (greedy [B, T], p [B, T], ok [B, T], out_len [B], out_path [B, max_depth],
-    out_bonus [B]).  ``p`` overrides the target probabilities (to replay a given set)."""
+    out_bonus [B]), everything computed here from the logits and the given draws."""
     B, T, V = logits.shape
     greedy = greedy_tokens(logits, logits_dtype)
-    if p is None:
-        p = node_probs(logits, logits_dtype, n_nodes, draft_tok, verify_row)
+    p = node_probs(logits, logits_dtype, n_nodes, draft_tok, verify_row)
     ok = np.zeros((B, T), dtype=bool)
     out_len = np.zeros(B, dtype=np.int32)
     out_path = np.full((B, max_depth), -1, dtype=np.int32)

@@ -2,12 +2,15 @@
 
 Bars: the greedy tokens bit-exact; each node's target probability within a
 relative 2e-5 of the float64 softmax; the accepted lengths, paths and
-correction tokens bit-exact against the oracle's scan run on the kernel's own
-probabilities (the decisions are float32 comparisons on both sides); and the
-kernel's decisions equal the oracle's float64-based ones except for nodes
-whose probability sits within that tolerance of the decision boundary.  Soft
-matching's acceptance rate over seeded uniforms is checked against the
-target probability with a binomial bound.
+correction tokens bit-exact against the oracle computed from the logits and
+the draws alone (its decisions are the real-valued comparisons, in float64).
+Thresholds and uniform draws are chosen a clear relative margin (1e-3, fifty
+times the probability tolerance) away from every node's decision boundary,
+so the float32 arithmetic of the kernel cannot flip a decision; a request
+whose nodes sit inside the band anyway (the workload-driven cases, whose
+inputs are not steered) is left out of the path comparison and counted, and
+such requests must be rare.  Soft matching's acceptance rate over seeded
+uniforms is checked against the target probability with a binomial bound.
 """
 
 import sys
@@ -81,36 +84,72 @@ def random_case(rng, B, T, V, dt, rows):
     return data, draft, parent, vrow, n_nodes
 
 
-def check(case_id, data, dt, n_nodes, draft, parent, vrow, max_depth, mode, threshold=0.0, dprob=None, unif=None):
+MARGIN = 1e-3     # relative distance of every steered decision from its boundary
+
+
+def edge_of(mode, threshold, dprob, unif, b, v):
+    """The value a node's probability is compared with."""
+    if mode == oracle.MODE_THRESHOLD:
+        return float(threshold)
+    return float(unif[b, v]) * float(dprob[b, v])
+
+
+def threshold_between(p):
+    """A threshold strictly between two adjacent distinct probabilities near the middle,
+    with at least MARGIN relative room on both sides."""
+    s = np.unique(p[np.isfinite(p) & (p > 0)])
+    order = sorted(range(1, len(s)), key=lambda i: abs(i - len(s) // 2))
+    for i in order:
+        lo, hi = s[i - 1], s[i]
+        if hi > lo * (1 + 4 * MARGIN):
+            return float(np.sqrt(lo * hi))
+    return 0.5
+
+
+def steer_uniforms(rng, p, dprob, n_nodes):
+    """Uniform draws, re-drawn where u * p_d would fall within MARGIN of p."""
+    unif = rng.random(p.shape).astype(np.float32)
+    for b in range(p.shape[0]):
+        for v in range(int(n_nodes[b])):
+            while np.isfinite(p[b, v]) and abs(float(unif[b, v]) * float(dprob[b, v]) - p[b, v]) <= \
+                    MARGIN * max(p[b, v], 1e-300):
+                unif[b, v] = np.float32(rng.random())
+    return unif
+
+
+def check(case_id, data, dt, n_nodes, draft, parent, vrow, max_depth, mode, threshold=0.0, dprob=None, unif=None,
+          steered=True):
     am, prob, ln, pth, bonus = run(data, dt, n_nodes, draft, parent, vrow, max_depth, mode, threshold, dprob, unif)
     greedy, p_ref, ok_ref, A_ref, path_ref, bonus_ref = oracle.prob_accept(
         data, dt, n_nodes, draft, parent, vrow, max_depth, mode, threshold, dprob, unif)
     B, T = draft.shape
-    band = 0
     for b in range(B):
         n = int(n_nodes[b])
         np.testing.assert_array_equal(am[b, :n], greedy[b, :n])
         assert (am[b, n:] == -1).all() and np.isnan(prob[b, n:]).all()
         np.testing.assert_allclose(prob[b, :n], p_ref[b, :n], rtol=P_RTOL, atol=1e-30)
-    # the kernel's scan on its own probabilities: exact
-    _, _, ok_k, A_k, path_k, bonus_k = oracle.prob_accept(data, dt, n_nodes, draft, parent, vrow, max_depth, mode,
-                                                         threshold, dprob, unif, p=prob.astype(np.float64))
-    np.testing.assert_array_equal(ln, A_k)
-    np.testing.assert_array_equal(pth, path_k)
-    np.testing.assert_array_equal(bonus, bonus_k)
-    # decisions from float64 probabilities differ only next to the boundary
+    # requests with a node whose probability lies within the band of its boundary
+    near = []
     for b in range(B):
         for v in range(int(n_nodes[b])):
-            if ok_k[b, v] != ok_ref[b, v]:
-                edge = threshold if mode == oracle.MODE_THRESHOLD else float(np.float32(unif[b, v]) *
-                                                                              np.float32(dprob[b, v]))
-                assert abs(p_ref[b, v] - edge) <= 2 * P_RTOL * max(abs(edge), 1e-30), (b, v)
-                band += 1
-    if band == 0:
-        np.testing.assert_array_equal(ln, A_ref)
-        np.testing.assert_array_equal(pth, path_ref)
-        np.testing.assert_array_equal(bonus, bonus_ref)
-    say(f"    {case_id}: accepted {ln.tolist()[:8]}, boundary nodes {band}")
+            # NaN rows, the unchecked root and the definitional zeros (a row or token out of
+            # range: exactly 0 on both sides) decide nothing near a boundary
+            if not np.isfinite(p_ref[b, v]) or p_ref[b, v] == 0.0 or (vrow is not None and vrow[b, v] == -1):
+                continue
+            edge = edge_of(mode, threshold, dprob, unif, b, v)
+            if abs(p_ref[b, v] - edge) <= 2 * P_RTOL * max(abs(edge), p_ref[b, v], 1e-300):
+                near.append(b)
+                break
+    if steered:
+        assert not near, f"steered inputs left requests {near} at the boundary"
+    else:
+        assert len(near) <= max(1, B // 8), f"too many boundary requests: {near}"
+    keep = [b for b in range(B) if b not in near]
+    np.testing.assert_array_equal(ln[keep], A_ref[keep])
+    np.testing.assert_array_equal(pth[keep], path_ref[keep])
+    np.testing.assert_array_equal(bonus[keep], bonus_ref[keep])
+    say(f"    {case_id}: accepted {ln.tolist()[:8]}, accepted nodes {int(ok_ref.sum())}, "
+        f"boundary requests {len(near)}")
 
 
 CASES = [
@@ -129,15 +168,14 @@ def test_prob_accept_parity(case, mode):
     rng = np.random.default_rng(len(cid) * 100 + B * 10 + mode)
     say(f"[gpu] prob accept {cid} mode {mode}")
     data, draft, parent, vrow, n_nodes = random_case(rng, B, T, V, dt, rows)
+    p = oracle.node_probs(data, dt, n_nodes, draft, vrow)
     if mode == oracle.MODE_THRESHOLD:
-        p = oracle.node_probs(data, dt, n_nodes, draft, vrow)
-        thr = float(np.nanmedian(p[p > 0])) if (p > 0).any() else 0.1
-        check(cid, data, dt, n_nodes, draft, parent, vrow, 8, mode, threshold=thr)
-        check(cid + "/t0", data, dt, n_nodes, draft, parent, vrow, 8, mode, threshold=0.0)
+        check(cid, data, dt, n_nodes, draft, parent, vrow, 8, mode, threshold=threshold_between(p))
+        check(cid + "/t0", data, dt, n_nodes, draft, parent, vrow, 8, mode, threshold=0.0, steered=False)
     else:
         dprob = rng.random((B, T)).astype(np.float32)
         dprob[:, ::7] = 0.0
-        unif = rng.random((B, T)).astype(np.float32)
+        unif = steer_uniforms(rng, p, dprob, n_nodes)
         check(cid, data, dt, n_nodes, draft, parent, vrow, 8, mode, dprob=dprob, unif=unif)
 
 
@@ -169,28 +207,34 @@ def test_planted_workload_threshold():
     x = wl.generate(cfg, B=4, L=(8, 8))
     for thr in (1e-3, 0.5):
         check(f"c3_planted/{thr}", x["logits"], "bf16", x["n_nodes"], x["draft_tok"], x["acc_parent"], None,
-              cfg.max_depth, oracle.MODE_THRESHOLD, threshold=thr)
+              cfg.max_depth, oracle.MODE_THRESHOLD, threshold=thr, steered=False)
 
 
 @pytest.mark.parametrize("rule", ["threshold", "soft"])
 def test_step_with_probability_acceptance(rule):
-    # the whole step (mask, attention, probability acceptance, commit) as the benchmark runs it
+    # the whole step (mask, attention, probability acceptance, commit) as the benchmark runs it,
+    # against the oracle computed from the logits and draws alone
     from masked_verification_attention_amd.step import VerifyStep
     cfg = wl.CONFIGS["c3_confu_8b"]
     x = wl.generate(cfg, B=3, L=(40, 80))
     rng = np.random.default_rng(5)
+    mode = oracle.MODE_THRESHOLD if rule == "threshold" else oracle.MODE_SOFT
     dprob = (rng.random(x["acc_parent"].shape) * 0.02).astype(np.float32)
-    unif = rng.random(x["acc_parent"].shape).astype(np.float32)
+    p0 = oracle.node_probs(x["logits"], "bf16", x["n_nodes"], x["draft_tok"], None)
+    unif = steer_uniforms(rng, p0, dprob, x["n_nodes"])
     st = VerifyStep(cfg, x, accept=rule, threshold=1e-3, draft_prob=dprob, uniform=unif)
     st.run()
     torch.cuda.synchronize()
-    mode = oracle.MODE_THRESHOLD if rule == "threshold" else oracle.MODE_SOFT
     prob = st.out_prob.cpu().numpy().astype(np.float64)
-    _, p_ref, _, _, _, _ = oracle.prob_accept(x["logits"], "bf16", x["n_nodes"], x["draft_tok"], x["acc_parent"],
-                                              None, st.max_depth, mode, 1e-3, dprob, unif)
+    _, p_ref, ok_ref, A, path, _ = oracle.prob_accept(x["logits"], "bf16", x["n_nodes"], x["draft_tok"],
+                                                      x["acc_parent"], None, st.max_depth, mode, 1e-3, dprob, unif)
     np.testing.assert_allclose(prob, p_ref, rtol=P_RTOL, atol=1e-30)
-    _, _, _, A, path, _ = oracle.prob_accept(x["logits"], "bf16", x["n_nodes"], x["draft_tok"], x["acc_parent"],
-                                             None, st.max_depth, mode, 1e-3, dprob, unif, p=prob)
+    # the threshold 1e-3 sits far from both the planted drafts (~1e-2) and the others (~1e-5)
+    n = x["n_nodes"]
+    for b in range(len(n)):
+        for v in range(int(n[b])):
+            edge = 1e-3 if mode == oracle.MODE_THRESHOLD else float(unif[b, v]) * float(dprob[b, v])
+            assert abs(p_ref[b, v] - edge) > MARGIN * max(edge, p_ref[b, v]), (b, v)
     np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
     np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
     kc, vc, L2 = oracle.commit_kv(x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"], A, path)
@@ -198,7 +242,7 @@ def test_step_with_probability_acceptance(rule):
     k_host, v_host = st.cache_host()
     np.testing.assert_array_equal(k_host, kc)
     np.testing.assert_array_equal(v_host, vc)
-    say(f"    {rule}: accepted {A.tolist()}")
+    say(f"    {rule}: accepted {A.tolist()} ({int(ok_ref.sum())} nodes pass)")
 
 
 def _edge_rows(V, rng):

@@ -56,10 +56,16 @@ def test_threshold_limits():
     assert ok.all() and (A == T).all()
     _, _, ok, A, _, bonus = oracle.prob_accept(logits, "f32", n, draft, parent, None, 8, oracle.MODE_THRESHOLD, 1.0)
     assert not ok.any() and (A == 0).all() and (bonus == -1).all()
-    # a threshold between two probabilities splits exactly there
-    t = float(np.median(p))
+    # a threshold between two adjacent distinct probabilities splits exactly there
+    s = np.unique(p)
+    t = float(0.5 * (s[len(s) // 2 - 1] + s[len(s) // 2]))
     _, _, ok, _, _, _ = oracle.prob_accept(logits, "f32", n, draft, parent, None, 8, oracle.MODE_THRESHOLD, t)
-    np.testing.assert_array_equal(ok, p.astype(np.float32) > np.float32(t))
+    np.testing.assert_array_equal(ok, p > t)
+    assert 0 < ok.sum() < ok.size
+    # a threshold equal to a probability does not accept it (strict comparison)
+    _, _, ok, _, _, _ = oracle.prob_accept(logits, "f32", n, draft, parent, None, 8, oracle.MODE_THRESHOLD,
+                                           float(s[0]))
+    assert not ok[p == s[0]].any() and ok[p > s[0]].all()
 
 
 def test_soft_limits():
@@ -78,6 +84,15 @@ def test_soft_limits():
     _, _, ok, A, _, _ = oracle.prob_accept(logits, "f32", n, draft, parent, None, 8, oracle.MODE_SOFT,
                                            draft_prob=np.zeros((B, T)), uniform=u)
     assert ok.all()                                        # a draft that never proposes x: accept if p_t > 0
+    # the decision is the real-valued u < p_t / p_d: just below and just above the ratio
+    r = p / 0.5
+    below = np.minimum(r * (1 - 1e-9), 0.999999)
+    _, _, ok, _, _, _ = oracle.prob_accept(logits, "f32", n, draft, parent, None, 8, oracle.MODE_SOFT,
+                                           draft_prob=np.full((B, T), 0.5), uniform=below)
+    assert ok.all()
+    _, _, ok, _, _, _ = oracle.prob_accept(logits, "f32", n, draft, parent, None, 8, oracle.MODE_SOFT,
+                                           draft_prob=np.full((B, T), 0.5), uniform=r * (1 + 1e-9))
+    assert not ok.any()
 
 
 @pytest.mark.parametrize("seed", range(60))
