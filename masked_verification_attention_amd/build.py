@@ -38,9 +38,7 @@ def hipcc() -> str:
     return path
 
 
-# the MFMA attention names the reserved m0 register as clobbered by its
-# direct-to-LDS load asm; the backend warns about exactly that
-EXTRA_FLAGS = {"attn_mfma.hip": ["-Wno-inline-asm"]}
+EXTRA_FLAGS = {}
 
 
 def _compile(src: str) -> str:

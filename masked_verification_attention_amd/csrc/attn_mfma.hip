@@ -121,13 +121,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // 16-byte direct-to-LDS load: lane i's 16 bytes from src land at LDS byte
-// address lds + 16 i.  Issued through asm so that the compiler does not
-// serialise the ring with its own conservative waits; completion is tracked
-// explicitly with wait_vmcnt.  m0 is named as clobbered; the compiler reserves
-// m0 and warns that it does not preserve it across the asm, which is what is
-// wanted (this file is built with -Wno-inline-asm for that warning).
+// address lds + 16 i (lds must be wave-uniform).  Issued through asm so that
+// the compiler does not serialise the ring with its own conservative waits;
+// completion is tracked explicitly with wait_vmcnt.  The LDS address is an
+// input bound to m0, so the compiler itself writes m0 before the load and
+// knows the register is in use.
 __device__ __forceinline__ void dma16(uint32_t lds, const char* src) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ void block_barrier() {
