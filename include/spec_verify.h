@@ -13,6 +13,8 @@
  *                       streams per tree node)
  *   spec_verify_attn    attention of the block's queries over
  *                       [soft prompt | cached prefix | block] under that mask
+ *   spec_verify_attn_noalloc  the same without a workspace argument (for
+ *                       callers that cannot allocate)
  *   spec_argmax_accept  per-node greedy token, longest accepted path
  *   spec_argmax_accept_rows  the same with explicit verification rows, an
  *                       explicit root and the correction token
@@ -40,7 +42,8 @@
  * Conventions (all entry points):
  *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
  *     stated otherwise.  The library allocates no memory and keeps no state
- *     between calls; calls are reentrant.
+ *     between calls; calls are reentrant (spec_verify_attn_noalloc aside,
+ *     which uses a scratch array the library holds per GPU).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued asynchronously; the functions never synchronise.  Values that
  *     depend on data (accepted lengths and paths, cache lengths) stay on the
@@ -85,6 +88,8 @@ typedef enum {
 #define SPEC_MAX_DEPTH 16      /* longest accepted path                    */
 #define SPEC_MAX_SOFT 256      /* soft-prompt rows                          */
 #define SPEC_MAX_TOPK 8        /* tokens per speculative stream in a draft  */
+/* device scratch spec_verify_attn_noalloc holds per GPU (32 MiB) */
+#define SPEC_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* acceptance rules of spec_prob_accept */
 #define SPEC_ACCEPT_THRESHOLD 1 /* [LA]: target probability of the draft > threshold          */
@@ -305,6 +310,37 @@ int spec_verify_attn(const spec_attn_desc* d, const void* q,
                      const uint32_t* mask_bits, const uint32_t* sp_bits, const int32_t* n_q,
                      float* out, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * spec_verify_attn_noalloc -- spec_verify_attn without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and kernels as spec_verify_attn minus
+ * (workspace, workspace_bytes).  The split-KV partials, when the schedule
+ * splits (automatic, or kv_splits > 0), go to a file-scope device array of
+ * SPEC_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; its device address is looked up once per device
+ * (hipGetSymbolAddress) on the first call that needs it, on the calling
+ * thread's current device, which must be the device of `stream`.  The call
+ * allocates nothing (no hipMalloc / hipFree).  The scratch needs no
+ * initialisation: every partial is written before it is read.
+ *
+ * All calls on one GPU share that array: two calls whose work overlaps on
+ * the device (different streams, no ordering between them) race and give
+ * unspecified results.  Calls ordered on one stream are safe.
+ *
+ * Errors: as spec_verify_attn; SPEC_EWORKSPACE when the call would need more
+ * than SPEC_NOALLOC_SCRATCH_BYTES of partials (spec_verify_attn_workspace
+ * gives the amount), checked before anything is enqueued; SPEC_EHIP when the
+ * scratch's address cannot be obtained.
+ */
+int spec_verify_attn_noalloc(const spec_attn_desc* d, const void* q,
+                             const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                             const void* k_blk, const void* v_blk,
+                             const void* k_soft, const void* v_soft,
+                             const uint32_t* mask_bits, const uint32_t* sp_bits, const int32_t* n_q,
+                             float* out, float* lse, void* stream);
 
 /*
  * spec_argmax_accept -- greedy verification of a draft tree.

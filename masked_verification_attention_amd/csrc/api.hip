@@ -8,7 +8,14 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.hpp"
+
+// Device scratch of spec_verify_attn_noalloc (split-KV partials), one copy per
+// GPU for the life of the process.  In host code `scratch` is only a symbol
+// handle: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -295,35 +302,39 @@ size_t spec_verify_attn_workspace(const spec_attn_desc* d) {
   return sv::plan_attn(*d).ws_bytes;
 }
 
-int spec_verify_attn(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
-                     const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
-                     const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
-                     const int32_t* n_q, float* out, float* lse, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of spec_verify_attn and spec_verify_attn_noalloc (the workspace aside).
+int check_attn_args(const char* fn, const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
+                    const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits, const int32_t* n_q,
+                    const float* out, const float* lse) {
   const int st = check_desc(d);
   if (st != SPEC_OK) return st;
-  if (d->B == 0) return ok();
+  if (d->B == 0) return SPEC_OK;
   REQUIRE(q && k_cache && v_cache && cache_len && k_blk && v_blk && mask_bits && n_q && out, SPEC_EINVAL,
-          "q, k_cache, v_cache, cache_len, k_blk, v_blk, mask_bits, n_q and out must be non-NULL");
+          "%s: q, k_cache, v_cache, cache_len, k_blk, v_blk, mask_bits, n_q and out must be non-NULL", fn);
   if (d->S > 0) {
-    REQUIRE(k_soft && v_soft && sp_bits, SPEC_EINVAL, "S = %d needs k_soft, v_soft and sp_bits", d->S);
+    REQUIRE(k_soft && v_soft && sp_bits, SPEC_EINVAL, "%s: S = %d needs k_soft, v_soft and sp_bits", fn, d->S);
   } else {
-    REQUIRE(!k_soft && !v_soft, SPEC_EINVAL, "k_soft / v_soft given with S = 0");
+    REQUIRE(!k_soft && !v_soft, SPEC_EINVAL, "%s: k_soft / v_soft given with S = 0", fn);
   }
   REQUIRE(aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(k_blk, 16) &&
               aligned(v_blk, 16) && aligned(out, 16) && aligned(k_soft, 16) && aligned(v_soft, 16),
-          SPEC_EINVAL, "q, caches, block, soft and out must be 16-byte aligned");
+          SPEC_EINVAL, "%s: q, caches, block, soft and out must be 16-byte aligned", fn);
   REQUIRE(aligned(cache_len, 4) && aligned(mask_bits, 4) && aligned(sp_bits, 4) && aligned(n_q, 4) &&
               aligned(lse, 4),
-          SPEC_EINVAL, "int32/uint32/float arrays must be 4-byte aligned");
+          SPEC_EINVAL, "%s: int32/uint32/float arrays must be 4-byte aligned", fn);
+  return SPEC_OK;
+}
 
-  const sv::AttnPlan plan = sv::plan_attn(*d);
-  if (plan.ws_bytes > 0) {
-    REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, SPEC_EWORKSPACE,
-            "workspace of %zu bytes needed, %zu given", plan.ws_bytes, workspace ? workspace_bytes : 0);
-    REQUIRE(aligned(workspace, 16), SPEC_EINVAL, "workspace must be 16-byte aligned");
-  }
-
+// Enqueue a validated call; `workspace` holds at least plan.ws_bytes bytes.
+int launch_verify_attn(const spec_attn_desc* d, const sv::AttnPlan& plan, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* cache_len, const void* k_blk, const void* v_blk,
+                       const void* k_soft, const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
+                       const int32_t* n_q, float* out, float* lse, void* workspace, void* stream) {
   sv::AttnArgs a{};
   a.B = d->B;
   a.Tq = d->Tq;
@@ -371,6 +382,75 @@ int spec_verify_attn(const spec_attn_desc* d, const void* q, const void* k_cache
     if (e != hipSuccess) return hip_status(e, "spec_verify_attn combine launch");
   }
   return ok();
+}
+
+// Device address of `scratch` on the calling thread's current device, looked up
+// once per device (each GPU holds its own copy at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "spec_verify_attn_noalloc: hipGetDevice");
+  REQUIRE(dev >= 0 && dev < kMaxDevices, SPEC_EUNSUPPORTED, "spec_verify_attn_noalloc: device %d >= %d", dev,
+          kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "spec_verify_attn_noalloc: hipGetSymbolAddress(scratch)");
+    REQUIRE(ptr != nullptr, SPEC_EHIP, "spec_verify_attn_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_attn(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
+                     const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
+                     const int32_t* n_q, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const int st = check_attn_args("spec_verify_attn", d, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft,
+                                 v_soft, mask_bits, sp_bits, n_q, out, lse);
+  if (st != SPEC_OK) return st;
+  if (d->B == 0) return ok();
+  const sv::AttnPlan plan = sv::plan_attn(*d);
+  if (plan.ws_bytes > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, SPEC_EWORKSPACE,
+            "workspace of %zu bytes needed, %zu given", plan.ws_bytes, workspace ? workspace_bytes : 0);
+    REQUIRE(aligned(workspace, 16), SPEC_EINVAL, "workspace must be 16-byte aligned");
+  }
+  return launch_verify_attn(d, plan, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft, mask_bits,
+                            sp_bits, n_q, out, lse, workspace, stream);
+}
+
+int spec_verify_attn_noalloc(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
+                             const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
+                             const int32_t* n_q, float* out, float* lse, void* stream) {
+  const int st = check_attn_args("spec_verify_attn_noalloc", d, q, k_cache, v_cache, cache_len, k_blk, v_blk,
+                                 k_soft, v_soft, mask_bits, sp_bits, n_q, out, lse);
+  if (st != SPEC_OK) return st;
+  if (d->B == 0) return ok();
+  const sv::AttnPlan plan = sv::plan_attn(*d);
+  REQUIRE(plan.ws_bytes <= (size_t)SPEC_NOALLOC_SCRATCH_BYTES, SPEC_EWORKSPACE,
+          "spec_verify_attn_noalloc: this call needs %zu bytes of split-KV scratch, more than the %zu the "
+          "library holds per GPU (use fewer splits, or spec_verify_attn with a workspace)",
+          plan.ws_bytes, (size_t)SPEC_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    const int sst = scratch_of_current_device(&ws);
+    if (sst != SPEC_OK) return sst;
+  }
+  return launch_verify_attn(d, plan, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft, mask_bits,
+                            sp_bits, n_q, out, lse, ws, stream);
 }
 
 int spec_argmax_accept(const void* logits, int32_t logits_dtype, int32_t B, int32_t T, int32_t V,

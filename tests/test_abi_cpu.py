@@ -223,3 +223,29 @@ def test_binding_refuses_host_tensors():
     host = torch.zeros(2, 8, dtype=torch.int32)
     with pytest.raises(ValueError, match="device"):
         bd.spec_build_mask(host, None, FAKE, 2, 8, FAKE, FAKE, stream=0)
+
+
+def test_noalloc_refuses_more_scratch_than_it_holds_before_any_hip_call():
+    # 64 requests x 8 kv-heads x 2048 rows x 8 splits of partials: far above the scratch size
+    desc = good_desc(B=64, Tq=256, Hq=64, Hkv=8, lmax=16384, strides=(16384 * 8 * 128, 8 * 128, 128), kv_splits=8)
+    need = bd.spec_verify_attn_workspace(desc)
+    assert need > bd.SPEC_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(bd.SpecError) as e:
+        bd.spec_verify_attn_noalloc(desc, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    None, stream=0)
+    assert e.value.status == bd.SPEC_EWORKSPACE
+    assert str(need) in str(e.value) and str(bd.SPEC_NOALLOC_SCRATCH_BYTES) in str(e.value)
+    # the argument checks are those of spec_verify_attn
+    with pytest.raises(bd.SpecError) as e:
+        bd.spec_verify_attn_noalloc(good_desc(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE + 4, None, stream=0)
+    assert e.value.status == bd.SPEC_EINVAL and "16-byte aligned" in str(e.value)
+    # B == 0 is a no-op that touches no device
+    bd.spec_verify_attn_noalloc(good_desc(B=0), None, None, None, None, None, None, None, None, None, None, None,
+                                None, None, stream=0)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SPEC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == bd.SPEC_NOALLOC_SCRATCH_BYTES
