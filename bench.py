@@ -225,7 +225,7 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=16, help="requests in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0)
-    ap.add_argument("--layout", choices=("bhld", "blhd"), default="bhld")
+    ap.add_argument("--layout", choices=("bhld", "blhd", "bhld_vt"), default="bhld")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-pmc", metavar="DIRS",

@@ -113,8 +113,27 @@ typedef struct {
                       [B, Hkv, lmax, D] contiguous: (Hkv*lmax*D, D, lmax*D). */
   int32_t kv_splits; /* 0 = automatic; else split each request's prefix into
                         this many key ranges (tuning and testing)             */
-  int32_t reserved;  /* must be 0                                             */
+  int32_t v_layout;  /* spec_v_layout of v_cache (K always uses the strides)  */
 } spec_attn_desc;
+
+/* Layout of the V cache (spec_attn_desc.v_layout).
+ *   SPEC_V_ROWS    V has K's layout: element (b, l, h, d) at
+ *                  b*kv_stride_b + l*kv_stride_l + h*kv_stride_h + d.
+ *   SPEC_V_TILE32  V is stored in tiles of 32 keys, each tile a contiguous
+ *                  [D/16][4][16][8] block -- head-dim block, key group, head dim
+ *                  within the block, key within the group -- so that every
+ *                  16 bytes is one operand of the attention's P*V matrix
+ *                  instruction.  Key l = 32t + k, head dim x of head h is at
+ *                  b*kv_stride_b + h*kv_stride_h + 32t*D
+ *                    + (x/16)*512 + g*128 + (x%16)*8 + e,
+ *                  g = (k%16)/4, e = k%4 + 4*(k/16) (a group holds keys
+ *                  4g..4g+3 and 16+4g..16+4g+3, the keys one lane's score
+ *                  accumulators hold).  Needs bf16, a head-major cache
+ *                  (kv_stride_l == D, so K is [B, Hkv, lmax, D] and V fills
+ *                  the same space) and lmax % 32 == 0.  spec_commit_kv and
+ *                  spec_argmax_accept_commit write accepted rows in this layout. */
+#define SPEC_V_ROWS 0
+#define SPEC_V_TILE32 1
 
 /*
  * spec_build_mask -- bit-packed visibility of block keys for each query row.

@@ -31,6 +31,8 @@ SPEC_MAX_DEPTH = 16
 SPEC_MAX_SOFT = 256
 SPEC_MAX_TOPK = 8
 SPEC_NOALLOC_SCRATCH_BYTES = 32 << 20
+SPEC_V_ROWS = 0
+SPEC_V_TILE32 = 1
 SPEC_ACCEPT_THRESHOLD = 1
 SPEC_ACCEPT_SOFT = 2
 
@@ -53,7 +55,7 @@ class AttnDesc(ctypes.Structure):
         ("B", ctypes.c_int32), ("Tq", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
         ("D", ctypes.c_int32), ("S", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
         ("lmax", ctypes.c_int64), ("kv_stride_b", ctypes.c_int64), ("kv_stride_l", ctypes.c_int64),
-        ("kv_stride_h", ctypes.c_int64), ("kv_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("kv_stride_h", ctypes.c_int64), ("kv_splits", ctypes.c_int32), ("v_layout", ctypes.c_int32),
     ]
 
 
@@ -137,9 +139,9 @@ def _check(status: int, func: str):
         raise SpecError(status, func, load().spec_last_error().decode())
 
 
-def make_desc(B, Tq, Hq, Hkv, D, S, dtype, lmax, strides, scale=0.0, kv_splits=0) -> AttnDesc:
+def make_desc(B, Tq, Hq, Hkv, D, S, dtype, lmax, strides, scale=0.0, kv_splits=0, v_layout=SPEC_V_ROWS) -> AttnDesc:
     sb, sl, sh = strides
-    return AttnDesc(B, Tq, Hq, Hkv, D, S, dtype, scale, lmax, sb, sl, sh, kv_splits, 0)
+    return AttnDesc(B, Tq, Hq, Hkv, D, S, dtype, scale, lmax, sb, sl, sh, kv_splits, v_layout)
 
 
 def spec_build_mask(attn_parent, sp_flag, n_q, B, Tq, mask_bits, sp_bits, stream=None):

@@ -70,7 +70,16 @@ int check_desc(const spec_attn_desc* d) {
   REQUIRE(d->kv_stride_l * es <= (int64_t(1) << 25), SPEC_EUNSUPPORTED,
           "kv_stride_l of %lld elements exceeds 32 MiB per cache row", (long long)d->kv_stride_l);
   REQUIRE(d->kv_splits >= 0 && d->kv_splits <= 64, SPEC_EINVAL, "kv_splits = %d outside [0, 64]", d->kv_splits);
-  REQUIRE(d->reserved == 0, SPEC_EINVAL, "reserved field must be 0");
+  REQUIRE(d->v_layout == SPEC_V_ROWS || d->v_layout == SPEC_V_TILE32, SPEC_EINVAL,
+          "v_layout = %d is not a spec_v_layout", d->v_layout);
+  if (d->v_layout == SPEC_V_TILE32) {
+    REQUIRE(d->dtype == SPEC_BF16, SPEC_EUNSUPPORTED, "v_layout SPEC_V_TILE32 needs bf16");
+    REQUIRE(d->kv_stride_l == d->D, SPEC_EINVAL,
+            "v_layout SPEC_V_TILE32 needs a head-major cache (kv_stride_l == D), got kv_stride_l = %lld",
+            (long long)d->kv_stride_l);
+    REQUIRE(d->lmax % 32 == 0, SPEC_EINVAL, "v_layout SPEC_V_TILE32 needs lmax %% 32 == 0, got lmax = %lld",
+            (long long)d->lmax);
+  }
   REQUIRE(isfinite(d->scale) && d->scale >= 0.f, SPEC_EINVAL, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
   REQUIRE((int64_t)d->B * d->Hkv <= 65535, SPEC_EUNSUPPORTED, "B * Hkv = %lld exceeds 65535",
           (long long)((int64_t)d->B * d->Hkv));
@@ -367,6 +376,7 @@ int launch_verify_attn(const spec_attn_desc* d, const sv::AttnPlan& plan, const 
   a.n_split = plan.n_split;
   a.row_chunks = plan.row_chunks;
   a.rows_per_wg = plan.rows_per_wg;
+  a.v_tiled = d->v_layout == SPEC_V_TILE32;
   if (plan.n_split > 1) {
     const size_t rows = (size_t)plan.n_split * d->B * d->Hkv * a.R;
     char* ws = static_cast<char*>(workspace);
@@ -485,8 +495,9 @@ int spec_commit_kv(const spec_attn_desc* d, void* k_cache, void* v_cache, const 
           SPEC_EINVAL, "int32 arrays must be 4-byte aligned");
   const hipError_t e =
       sv::launch_commit(d->B, d->Tq, d->Hkv, d->D, esize_of(d->dtype), d->lmax, d->kv_stride_b,
-                        d->kv_stride_l, d->kv_stride_h, k_cache, v_cache, cache_len_in, cache_len_out, k_blk,
-                        v_blk, out_len, out_path, max_depth, static_cast<hipStream_t>(stream));
+                        d->kv_stride_l, d->kv_stride_h, d->v_layout == SPEC_V_TILE32, k_cache, v_cache,
+                        cache_len_in, cache_len_out, k_blk, v_blk, out_len, out_path, max_depth,
+                        static_cast<hipStream_t>(stream));
   return hip_status(e, "spec_commit_kv launch");
 }
 
@@ -523,8 +534,9 @@ int spec_argmax_accept_commit(const void* logits, int32_t logits_dtype, int32_t 
   if (e != hipSuccess) return hip_status(e, "argmax launch");
   sv::AcceptRule greedy{};
   sv::CommitArgs c{1, d->Tq, d->Hkv, d->D, esize_of(d->dtype), d->lmax, d->kv_stride_b, d->kv_stride_l,
-                   d->kv_stride_h, static_cast<char*>(k_cache), static_cast<char*>(v_cache), cache_len_in,
-                   cache_len_out, static_cast<const char*>(k_blk), static_cast<const char*>(v_blk)};
+                   d->kv_stride_h, d->v_layout == SPEC_V_TILE32, static_cast<char*>(k_cache),
+                   static_cast<char*>(v_cache), cache_len_in, cache_len_out, static_cast<const char*>(k_blk),
+                   static_cast<const char*>(v_blk)};
   e = sv::launch_accept(B, T, n_nodes, draft_tok, acc_parent, verify_row, out_argmax, max_depth, out_len, out_path,
                         out_bonus, greedy, c, s);
   return hip_status(e, "acceptance + commit launch");

@@ -33,16 +33,20 @@
 //   soft keys and the block rows.  Segments are tiled separately, so prefix
 //   tiles need no mask except the ragged tail.  Each group copies its own
 //   tiles straight from HBM into rings of LDS slots (one for K, one for V) with
-//   16-byte direct-to-LDS loads, three steps ahead of the compute; a wave
-//   issues its share of a step's loads in its matrix half, after its fragment
-//   reads and before its matrix instructions.  K and V sit row-major in a slot with 16-byte chunk c of key row k stored at chunk
-//   position c ^ swz(k), an XOR map chosen so that both read patterns below are
-//   free of bank conflicts:
+//   16-byte direct-to-LDS loads, three steps ahead of the compute (the first
+//   three steps' loads go out before the setup loads); a wave issues its share
+//   of a step's loads in its matrix half, after its fragment reads and before
+//   its matrix instructions.  Row-major tiles (K, and V unless the cache keeps
+//   V transposed) sit in a slot with 16-byte chunk c of key row k stored at
+//   chunk position c ^ swz(k):
 //     S^T = K Q^T : K is the A operand, one 16-byte read per lane;
 //     O^T = V^T P^T : V^T is the A operand, built by the transposing 64-bit
 //                     LDS read (lane j of a 16-lane group receives element
 //                     j % 4 of the 8 bytes addressed by lane 4e + j / 4 of its
 //                     group, for e = 0..3).
+//   A cache whose V is stored in fragment-major 32-key tiles (SPEC_V_TILE32)
+//   is copied to LDS as it is, and each lane reads its V^T operand with one
+//   linear 16-byte read (soft and block tiles stay row-major).
 //   With S^T and O^T every lane holds one query row (lane % 16) for all its
 //   values: the row's 8 scores of a tile become the P operand directly (the
 //   contraction order over keys is permuted the same way in V^T), and the
@@ -136,7 +140,7 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, int NB>
+template <int D, int NB, bool VT>
 __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   using C = MfmaCfg<D, NB>;
   constexpr int DC = D / 32;   // k-chunks of S^T = K Q^T
@@ -166,7 +170,8 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 
   const int L = (int)min<int64_t>(max(a.cache_len[b], 0), a.lmax);
   const int nq = clampi(a.n_q[b], 0, a.Tq);
-  const int keys_per_split = (L + a.n_split - 1) / a.n_split;
+  // split boundaries on 32-key multiples, so a split's prefix tiles are the cache's tiles
+  const int keys_per_split = (((L + a.n_split - 1) / a.n_split) + C::TK - 1) / C::TK * C::TK;
   const int ks = min(L, split * keys_per_split);
   const int ke = min(L, ks + keys_per_split);
   const bool last = split == a.n_split - 1;
@@ -174,6 +179,97 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   const int nts = last ? (a.S + C::TK - 1) / C::TK : 0;
   const int ntb = last ? (nq + C::TK - 1) / C::TK : 0;
   const int nt = ntp + nts + ntb;
+
+  // ---- direct-to-LDS tile loads.  Group g's "step u loads" are what it reads
+  // at step u: K of its tile 2u+g (scored at step u) and V of its tile 2u+g-2
+  // (whose P*V runs at step u).  Waves 0..3 and 4..7 of the group split the K
+  // and V streams, LPS 1 KB wave loads each.
+  const char* kc = static_cast<const char*>(a.k_cache) + ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
+  const char* vc = static_cast<const char*>(a.v_cache) + ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
+  const char* kblk = static_cast<const char*>(a.k_blk) + ((int64_t)b * a.Tq * a.Hkv + h) * D * 2;
+  const char* vblk = static_cast<const char*>(a.v_blk) + ((int64_t)b * a.Tq * a.Hkv + h) * D * 2;
+  const char* ksoft = static_cast<const char*>(a.k_soft) + (int64_t)h * D * 2;
+  const char* vsoft = static_cast<const char*>(a.v_soft) + (int64_t)h * D * 2;
+  const int gw = wave & 3;                        // wave within its group
+  const bool load_v = (gw * C::LPS) / C::LPT >= 1;   // first half of the group loads K, second V
+  const int lrow = lane / C::CH;               // key row within the wave's 1 KB load
+  const int lpos = lane % C::CH;               // chunk position the lane fills
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_char*)ring;
+  const char* const kring = ring;
+  const char* const vring = ring + C::NSK * C::TILEB;
+  int lane_row[C::LPS], lane_off[C::LPS], lane_dst[C::LPS];
+#pragma unroll
+  for (int j = 0; j < C::LPS; ++j) {
+    const int ii = (gw * C::LPS + j) % C::LPT;
+    lane_row[j] = ii * C::RPI + lrow;
+    lane_off[j] = (lpos ^ C::swz(lane_row[j])) * 16;
+    lane_dst[j] = ii * 1024;
+  }
+  // A transposed V tile (SPEC_V_TILE32) is stored fragment-major: 1 KB piece
+  // db holds head dims 16 db .. +15, and its 16-byte chunk i is the P*V operand
+  // of lane i -- head dim 16 db + i % 16, the 8 keys 4 g + (0..3) and
+  // 16 + 4 g + (0..3) with g = i / 16, the keys the lane's score accumulators
+  // hold.  The tile is copied to LDS as it is (lane i's 16 bytes of a wave load
+  // land at byte 16 i, as the hardware places them), and the fragment read is
+  // linear: 195 B/clk per CU measured, against 154 for the transposing read of
+  // a row-major tile.
+  const int lane_vt = lane * 16;
+  // Rows past a segment's end are clamped to its last key and masked in the
+  // compute.  A tile past the end still issues its loads (the last tile again,
+  // into the slot that tile index maps to, which nothing reads): the waits
+  // below count loads, and a wait for "all but the newest step's loads" only
+  // covers an older step if the newer one really issued its share.  Tiles
+  // before the start (V in the first two steps) issue nothing; a non-empty
+  // step always follows them.
+  struct TileSrc {
+    const char* base;
+    int stride, nvalid;
+    uint32_t slot;
+    bool on, vt;      // vt: a transposed V tile of the prefix (read whole, no row clamp)
+  };
+  auto tile_src = [&](int u) __attribute__((always_inline)) {
+    TileSrc r;
+    const int tslot = 2 * u + grp - (load_v ? 2 : 0);
+    r.on = tslot >= 0;
+    r.vt = false;
+    const int t = min(max(tslot, 0), nt - 1);
+    if (t < ntp) {
+      r.vt = VT && load_v;
+      const int key0 = ks + t * C::TK;
+      r.base = (load_v ? vc : kc) + (int64_t)key0 * a.sl * 2;
+      r.stride = (int)(a.sl * 2);
+      r.nvalid = ke - key0;
+    } else if (t < ntp + nts) {
+      const int key0 = (t - ntp) * C::TK;
+      r.base = (load_v ? vsoft : ksoft) + (int64_t)key0 * a.Hkv * D * 2;
+      r.stride = a.Hkv * D * 2;
+      r.nvalid = a.S - key0;
+    } else {
+      const int key0 = (t - ntp - nts) * C::TK;
+      r.base = (load_v ? vblk : kblk) + (int64_t)key0 * a.Hkv * D * 2;
+      r.stride = a.Hkv * D * 2;
+      r.nvalid = nq - key0;
+    }
+    r.slot = ring_lds + (load_v ? (C::NSK + max(tslot, 0) % C::NSV) : (max(tslot, 0) % C::NSK)) * C::TILEB;
+    return r;
+  };
+  auto issue_one = [&](const TileSrc& r, int j) __attribute__((always_inline)) {
+    if (!r.on) return;
+    const int rel = min(lane_row[j], r.nvalid - 1);
+    dma16(r.slot + lane_dst[j], r.base + (r.vt ? lane_dst[j] + lane_vt : rel * r.stride + lane_off[j]));
+  };
+  auto issue_step = [&](int u) __attribute__((always_inline)) {
+    const TileSrc r = tile_src(u);
+#pragma unroll
+    for (int j = 0; j < C::LPS; ++j) issue_one(r, j);
+  };
+
+  // The first steps' tiles go out before the setup loads below, so their HBM
+  // latency overlaps that of the queries and mask words instead of following it.
+  if (nt > 0) {
+#pragma unroll
+    for (int u = 0; u < C::P / 2; ++u) issue_step(u);
+  }
 
   // ---- rows: mask words of the workgroup's rows into LDS; this lane's rows
   const int row0 = chunk_id * C::ROWS;
@@ -205,79 +301,6 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     }
   }
 
-  // ---- direct-to-LDS tile loads.  Group g's "step u loads" are what it reads
-  // at step u: K of its tile 2u+g (scored at step u) and V of its tile 2u+g-2
-  // (whose P*V runs at step u).  Waves 0..3 and 4..7 of the group split the K
-  // and V streams, LPS 1 KB wave loads each.
-  const char* kc = static_cast<const char*>(a.k_cache) + ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
-  const char* vc = static_cast<const char*>(a.v_cache) + ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
-  const char* kblk = static_cast<const char*>(a.k_blk) + ((int64_t)b * a.Tq * a.Hkv + h) * D * 2;
-  const char* vblk = static_cast<const char*>(a.v_blk) + ((int64_t)b * a.Tq * a.Hkv + h) * D * 2;
-  const char* ksoft = static_cast<const char*>(a.k_soft) + (int64_t)h * D * 2;
-  const char* vsoft = static_cast<const char*>(a.v_soft) + (int64_t)h * D * 2;
-  const int gw = wave & 3;                        // wave within its group
-  const bool load_v = (gw * C::LPS) / C::LPT >= 1;   // first half of the group loads K, second V
-  const int lrow = lane / C::CH;               // key row within the wave's 1 KB load
-  const int lpos = lane % C::CH;               // chunk position the lane fills
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_char*)ring;
-  const char* const kring = ring;
-  const char* const vring = ring + C::NSK * C::TILEB;
-  int lane_row[C::LPS], lane_off[C::LPS], lane_dst[C::LPS];
-#pragma unroll
-  for (int j = 0; j < C::LPS; ++j) {
-    const int ii = (gw * C::LPS + j) % C::LPT;
-    lane_row[j] = ii * C::RPI + lrow;
-    lane_off[j] = (lpos ^ C::swz(lane_row[j])) * 16;
-    lane_dst[j] = ii * 1024;
-  }
-  // Rows past a segment's end are clamped to its last key and masked in the
-  // compute.  A tile past the end still issues its loads (the last tile again,
-  // into the slot that tile index maps to, which nothing reads): the waits
-  // below count loads, and a wait for "all but the newest step's loads" only
-  // covers an older step if the newer one really issued its share.  Tiles
-  // before the start (V in the first two steps) issue nothing; a non-empty
-  // step always follows them.
-  struct TileSrc {
-    const char* base;
-    int stride, nvalid;
-    uint32_t slot;
-    bool on;
-  };
-  auto tile_src = [&](int u) __attribute__((always_inline)) {
-    TileSrc r;
-    const int tslot = 2 * u + grp - (load_v ? 2 : 0);
-    r.on = tslot >= 0;
-    const int t = min(max(tslot, 0), nt - 1);
-    if (t < ntp) {
-      const int key0 = ks + t * C::TK;
-      r.base = (load_v ? vc : kc) + (int64_t)key0 * a.sl * 2;
-      r.stride = (int)(a.sl * 2);
-      r.nvalid = ke - key0;
-    } else if (t < ntp + nts) {
-      const int key0 = (t - ntp) * C::TK;
-      r.base = (load_v ? vsoft : ksoft) + (int64_t)key0 * a.Hkv * D * 2;
-      r.stride = a.Hkv * D * 2;
-      r.nvalid = a.S - key0;
-    } else {
-      const int key0 = (t - ntp - nts) * C::TK;
-      r.base = (load_v ? vblk : kblk) + (int64_t)key0 * a.Hkv * D * 2;
-      r.stride = a.Hkv * D * 2;
-      r.nvalid = nq - key0;
-    }
-    r.slot = ring_lds + (load_v ? (C::NSK + max(tslot, 0) % C::NSV) : (max(tslot, 0) % C::NSK)) * C::TILEB;
-    return r;
-  };
-  auto issue_one = [&](const TileSrc& r, int j) __attribute__((always_inline)) {
-    if (!r.on) return;
-    const int rel = min(lane_row[j], r.nvalid - 1);
-    dma16(r.slot + lane_dst[j], r.base + (rel * r.stride + lane_off[j]));
-  };
-  auto issue_step = [&](int u) __attribute__((always_inline)) {
-    const TileSrc r = tile_src(u);
-#pragma unroll
-    for (int j = 0; j < C::LPS; ++j) issue_one(r, j);
-  };
-
   float mrun[NB], lrun[NB], negm[NB];
   f32x4 o[NB][DB];
 #pragma unroll
@@ -290,7 +313,8 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   }
   const int lx16 = ((lane ^ 16) << 2), lx32 = ((lane ^ 32) << 2);   // byte lane addresses for permutes
 
-  // setup loads (queries, flags, mask words) must land before the ring's vmcnt accounting starts
+  // setup loads (queries, flags, mask words) must land before the ring's vmcnt
+  // accounting starts; the first steps' tiles, issued before them, land with them
   __builtin_amdgcn_s_waitcnt(0);
   block_barrier();
 
@@ -309,9 +333,6 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) st[nb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int u = 0; u < C::P / 2; ++u) issue_step(u);
-
     // step s: wait for step s's loads, free the slots read at step s-1, refill
     auto begin_step = [&](int s) __attribute__((always_inline)) {
       wait_vmcnt<(C::P / 2 - 1) * C::LPS>();
@@ -361,6 +382,32 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
           vw[2 * cc + 1] = w2[1];
         }
         vf[db] = as_bf16x8(u32x4{vw[0], vw[1], vw[2], vw[3]});
+      }
+    };
+    // V^T fragments of a transposed tile tp: one linear 16-byte read per head-dim block
+    auto read_vt = [&](int tp, bf16x8 (&vf)[DB]) __attribute__((always_inline)) {
+      const char* slotV = vring + (tp % C::NSV) * C::TILEB + lane * 16;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vf[db] = as_bf16x8(*reinterpret_cast<const u32x4*>(slotV + db * 1024));
+    };
+    // zero the values of keys at or past lim (the ragged last tile of a
+    // transposed prefix: cache slots past the length may hold anything, NaN
+    // included, and a zero probability does not cancel a NaN in the product).
+    // Element e of the lane's fragment is key 4 q4 + e (e < 4) or 16 + 4 q4 + e - 4.
+    auto clip_vt = [&](bf16x8 (&vf)[DB], int lim) __attribute__((always_inline)) {
+      const int nlo = clampi(lim - 4 * q4, 0, 4), nhi = clampi(lim - 16 - 4 * q4, 0, 4);
+      u32x4 keep;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int n = w < 2 ? nlo : nhi, e = 2 * (w & 1);
+        keep[w] = (e < n ? 0x0000ffffu : 0u) | (e + 1 < n ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        u32x4 v;
+        __builtin_memcpy(&v, &vf[db], 16);
+        v &= keep;
+        vf[db] = as_bf16x8(v);
       }
     };
     // O^T += V^T P^T
@@ -487,8 +534,15 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         scores(kf, st);
       }
       if (s >= 1 && t - 2 < nt) {
+        const int tp = t - 2;
         bf16x8 vf[DB];
-        read_v(t - 2, vf);
+        if (VT && tp < ntp) {
+          read_vt(tp, vf);
+          const int lim = ke - (ks + tp * C::TK);
+          if (lim < C::TK) clip_vt(vf, lim);
+        } else {
+          read_v(tp, vf);
+        }
         pv(vf);
       }
     };
@@ -501,6 +555,29 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     };
     // own tiles 2s+g (scored and softmaxed) and 2s+g-2 (in P*V) are full prefix
     // tiles and 2s+g is not the group's first: no masks, no branches
+    // the matrix instructions of a hot step in issue order: scores (nb, kb, dc),
+    // then P*V (db, nb); mat_part issues those with index in [LO, HI)
+    auto mat_part = [&](const bf16x8 (&kf)[2][DC], const bf16x8 (&vf)[DB], auto LO, auto HI)
+        __attribute__((always_inline)) {
+      constexpr int lo = decltype(LO)::value, hi = decltype(HI)::value;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) {
+            const int idx = (nb * 2 + kb) * DC + dc;
+            if (idx >= lo && idx < hi)
+              st[nb][kb] = mfma16x16x32(kf[kb][dc], qf[nb][dc], dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : st[nb][kb]);
+          }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int idx = NB * 2 * DC + db * NB + nb;
+          if (idx >= lo && idx < hi) o[nb][db] = mfma16x16x32(vf[db], pf[nb], o[nb][db]);
+        }
+    };
     auto hot_step = [&](int s) __attribute__((always_inline)) {
       begin_step(s);
       const TileSrc src = tile_src(s + C::P / 2);
@@ -509,16 +586,31 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       // here they measured a little faster than spread through the softmax half)
       bf16x8 kf[2][DC], vf[DB];
       read_k(2 * s + grp, kf);
-      read_v(2 * s + grp - 2, vf);
+      if constexpr (VT)
+        read_vt(2 * s + grp - 2, vf);
+      else
+        read_v(2 * s + grp - 2, vf);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
-      scores(kf, st);
-      pv(vf);
+      // The barrier that hands the matrix cores to the other group goes after
+      // the first 12 of the step's 32 matrix instructions (pinned: the matrix
+      // instructions touch no memory, so the compiler would move them across
+      // it freely).  The rest then overlap the other group's fragment reads.
+      // Measured on the headline workload against other positions (0..32) and
+      // against the compiler's own placement, which varies with the code
+      // around it: 12 was fastest (78 us against 82-103).
+      constexpr int kMat = NB * 2 * DC + DB * NB;
+      constexpr int kAt = 12 < kMat ? 12 : kMat;
+      mat_part(kf, vf, std::integral_constant<int, 0>{}, std::integral_constant<int, kAt>{});
+      __builtin_amdgcn_sched_barrier(0);
       block_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      mat_part(kf, vf, std::integral_constant<int, kAt>{}, std::integral_constant<int, kMat>{});
       // the softmax half takes issue priority over the other group's wave on
       // the same SIMD, whose matrix instructions keep the matrix core busy
-      // meanwhile (measured 8-12% faster than equal priority)
+      // meanwhile (measured 4-12% faster than equal priority or a raised
+      // priority for the matrix instructions)
       __builtin_amdgcn_s_setprio(1);
       softmax_full(false);
       __builtin_amdgcn_sched_barrier(0);
@@ -605,13 +697,18 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
   const int64_t nwg = (int64_t)a.n_split * a.row_chunks * a.B * a.Hkv;
   const dim3 grid((unsigned)nwg);
   const dim3 block(512);
-  if (a.rows_per_wg == 128) {
-    if (a.D == 128) hipLaunchKernelGGL((k_attn_mfma<128, 2>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<64, 2>), grid, block, 0, st, a);
-  } else {
-    if (a.D == 128) hipLaunchKernelGGL((k_attn_mfma<128, 1>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<64, 1>), grid, block, 0, st, a);
-  }
+  auto go = [&](auto vt) {
+    constexpr bool VT = decltype(vt)::value;
+    if (a.rows_per_wg == 128) {
+      if (a.D == 128) hipLaunchKernelGGL((k_attn_mfma<128, 2, VT>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k_attn_mfma<64, 2, VT>), grid, block, 0, st, a);
+    } else {
+      if (a.D == 128) hipLaunchKernelGGL((k_attn_mfma<128, 1, VT>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((k_attn_mfma<64, 1, VT>), grid, block, 0, st, a);
+    }
+  };
+  if (a.v_tiled) go(std::true_type{});
+  else go(std::false_type{});
   return hipGetLastError();
 }
 

@@ -22,11 +22,11 @@ __global__ __launch_bounds__(kCommitThreads) void k_commit(CommitArgs c, const i
 }
 
 hipError_t launch_commit(int B, int Tq, int Hkv, int D, int esize, int64_t lmax, int64_t sb,
-                         int64_t sl, int64_t sh, void* k_cache, void* v_cache,
+                         int64_t sl, int64_t sh, int v_tiled, void* k_cache, void* v_cache,
                          const int32_t* cache_len_in, int32_t* cache_len_out, const void* k_blk,
                          const void* v_blk, const int32_t* out_len, const int32_t* out_path,
                          int max_depth, hipStream_t st) {
-  CommitArgs c{1, Tq, Hkv, D, esize, lmax, sb, sl, sh, static_cast<char*>(k_cache), static_cast<char*>(v_cache),
+  CommitArgs c{1, Tq, Hkv, D, esize, lmax, sb, sl, sh, v_tiled, static_cast<char*>(k_cache), static_cast<char*>(v_cache),
                cache_len_in, cache_len_out, static_cast<const char*>(k_blk), static_cast<const char*>(v_blk)};
   hipLaunchKernelGGL(k_commit, dim3(B), dim3(kCommitThreads), 0, st, c, out_len, out_path, max_depth);
   return hipGetLastError();

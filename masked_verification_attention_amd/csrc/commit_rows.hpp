@@ -46,7 +46,28 @@ __device__ __forceinline__ void commit_rows(int b, const CommitArgs& c, int A, c
     for (int u = 0; u < kU; ++u) {
       if (on[u]) {
         *reinterpret_cast<u32x4*>(c.k_cache + dst[u]) = kx[u];
-        *reinterpret_cast<u32x4*>(c.v_cache + dst[u]) = vx[u];
+        if (!c.v_tiled) {
+          *reinterpret_cast<u32x4*>(c.v_cache + dst[u]) = vx[u];
+        } else {
+          // fragment-major 32-key tiles (head-major, sl == D): key l = 32 t + k,
+          // dim x at (l - k) * D + (x / 16) * 512 + g * 128 + (x % 16) * 8 + e
+          // within the head's range, with g = (k % 16) / 4, e = k % 4 + 4 (k / 16)
+          const int idx = i0 + u * blockDim.x;
+          const int d = idx / row_chunks;
+          const int ch = idx % row_chunks;
+          const int h = ch / head_chunks, cc = ch % head_chunks;
+          const int64_t l = L + d;
+          const int k = (int)(l % 32);
+          const int g = (k & 15) >> 2, e = (k & 3) + 4 * (k >> 4);
+          const int64_t base = (int64_t)b * c.sb + (int64_t)h * c.sh + (l - k) * c.D + g * 128 + e;
+          uint16_t e16[8];
+          __builtin_memcpy(e16, &vx[u], 16);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int x = cc * 8 + j;
+            reinterpret_cast<uint16_t*>(c.v_cache)[base + (x >> 4) * 512 + (x & 15) * 8] = e16[j];
+          }
+        }
       }
     }
   }

@@ -37,6 +37,7 @@ struct AttnArgs {
   int n_split;
   int row_chunks;                   // MFMA path: row chunks per (request, kv-head)
   int rows_per_wg;                  // MFMA path: 64 or 128 rows per workgroup
+  int v_tiled;                      // V cache in SPEC_V_TILE32 layout (MFMA path only)
 };
 
 enum AttnPath { PATH_VALU = 0, PATH_MFMA = 1 };
@@ -71,6 +72,7 @@ struct CommitArgs {
   int enabled;              // fused form: 0 = acceptance only
   int Tq, Hkv, D, esize;
   int64_t lmax, sb, sl, sh; // cache capacity and element strides
+  int v_tiled;              // V cache in SPEC_V_TILE32 layout
   char* k_cache;
   char* v_cache;
   const int32_t* cache_len_in;
@@ -99,7 +101,7 @@ hipError_t launch_accept(int B, int T, const int32_t* n_nodes, const int32_t* dr
                          int max_depth, int32_t* out_len, int32_t* out_path, int32_t* out_bonus,
                          const AcceptRule& rule, const CommitArgs& commit, hipStream_t st);
 hipError_t launch_commit(int B, int Tq, int Hkv, int D, int esize, int64_t lmax, int64_t sb,
-                         int64_t sl, int64_t sh, void* k_cache, void* v_cache,
+                         int64_t sl, int64_t sh, int v_tiled, void* k_cache, void* v_cache,
                          const int32_t* cache_len_in, int32_t* cache_len_out, const void* k_blk,
                          const void* v_blk, const int32_t* out_len, const int32_t* out_path,
                          int max_depth, hipStream_t st);

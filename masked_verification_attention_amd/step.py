@@ -22,6 +22,11 @@ from .workloads import VerifyConfig
 
 DTYPE_CODE = {"f32": bd.SPEC_F32, "bf16": bd.SPEC_BF16}
 
+# SPEC_V_TILE32: a 32-key tile is [D/16][4][16][8] (head-dim block, key group g, head dim in the
+# block, key slot e); key k of the tile is at group/slot position 8 g + e = VT_POS_OF[k]
+VT_POS_OF = [8 * ((k % 16) // 4) + k % 4 + 4 * (k // 16) for k in range(32)]
+VT_KEY_AT = [VT_POS_OF.index(p) for p in range(32)]
+
 
 def to_device(x: np.ndarray, dtype: str, device) -> torch.Tensor:
     """Upload a generator array; bf16 arrays arrive as uint16 bit patterns."""
@@ -51,9 +56,11 @@ class VerifyStep:
                  scale: float = 0.0, max_depth: Optional[int] = None, layout: str = "blhd",
                  accept: str = "greedy", threshold: float = 1e-3, draft_prob=None, uniform=None):
         """``layout`` of the K/V cache in HBM: "blhd" = [B, lmax, Hkv, D] (token-major, the
-        generator's order) or "bhld" = [B, Hkv, lmax, D] (head-major).  Both are passed to
-        the library through the descriptor's strides; ``cache_host()`` returns the
-        cache in the generator's order either way.  ``accept`` selects the acceptance rule
+        generator's order), "bhld" = [B, Hkv, lmax, D] (head-major), or "bhld_vt" = K head-major
+        and V in transposed 32-key tiles [B, Hkv, lmax/32, D, 32] (SPEC_V_TILE32; lmax is
+        rounded up to a multiple of 32, the extra slots holding NaN like every unused slot).
+        The strides and V layout go to the library through the descriptor; ``cache_host()``
+        returns the cache in the generator's order and capacity either way.  ``accept`` selects the acceptance rule
         of ``run()``: "greedy" (hard matching), "threshold" (target probability above
         ``threshold``) or "soft" (soft matching with the given ``draft_prob`` and
         ``uniform`` arrays [B, T])."""
@@ -67,14 +74,28 @@ class VerifyStep:
         self.lmax = x["k_cache"].shape[1]
         self.max_depth = int(max_depth if max_depth is not None else min(cfg.max_depth, bd.SPEC_MAX_DEPTH))
         self.q = to_device(x["q"], dt, dev)
-        if layout not in ("blhd", "bhld"):
+        if layout not in ("blhd", "bhld", "bhld_vt"):
             raise ValueError(layout)
         self.layout = layout
+        self.lmax_gen = self.lmax
         self.k_cache = to_device(x["k_cache"], dt, dev)
         self.v_cache = to_device(x["v_cache"], dt, dev)
-        if layout == "bhld":
+        if layout == "bhld_vt":
+            pad = (-self.lmax) % 32
+            if pad:
+                fill = torch.full((self.B, pad) + tuple(self.k_cache.shape[2:]), float("nan"),
+                                  dtype=self.k_cache.dtype, device=dev)
+                self.k_cache = torch.cat([self.k_cache, fill], dim=1)
+                self.v_cache = torch.cat([self.v_cache, fill], dim=1)
+                self.lmax += pad
+        if layout in ("bhld", "bhld_vt"):
             self.k_cache = self.k_cache.permute(0, 2, 1, 3).contiguous()
             self.v_cache = self.v_cache.permute(0, 2, 1, 3).contiguous()
+        if layout == "bhld_vt":
+            B_, H_, L_, D_ = self.v_cache.shape
+            tiles = self.v_cache.reshape(B_, H_, L_ // 32, 32, D_)[:, :, :, VT_KEY_AT, :]   # [.., pos, D]
+            tiles = tiles.reshape(B_, H_, L_ // 32, 4, 8, D_ // 16, 16)                     # [.., g, e, db, r]
+            self.v_cache = tiles.permute(0, 1, 2, 5, 3, 6, 4).contiguous()                 # [.., db, g, r, e]
         self.k_blk = to_device(x["k_blk"], dt, dev)
         self.v_blk = to_device(x["v_blk"], dt, dev)
         self.k_soft = to_device(x["k_soft"], dt, dev) if cfg.S else None
@@ -128,16 +149,24 @@ class VerifyStep:
         strides = ((self.lmax * Hkv * D, Hkv * D, D) if layout == "blhd"
                    else (Hkv * self.lmax * D, D, self.lmax * D))
         self.desc = bd.make_desc(self.B, self.Tq, cfg.Hq, Hkv, D, cfg.S, DTYPE_CODE[dt], self.lmax,
-                                 strides, scale=scale, kv_splits=kv_splits)
+                                 strides, scale=scale, kv_splits=kv_splits,
+                                 v_layout=bd.SPEC_V_TILE32 if layout == "bhld_vt" else bd.SPEC_V_ROWS)
         self.ws_bytes = bd.spec_verify_attn_workspace(self.desc)
         self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
                           if self.ws_bytes else None)
 
-    def cache_host(self):
-        """(k_cache, v_cache) as host arrays in the generator's [B, lmax, Hkv, D] order."""
+    def cache_host(self, full: bool = False):
+        """(k_cache, v_cache) as host arrays in the generator's [B, lmax, Hkv, D] order
+        (``full``: with the slots added to round lmax up to a multiple of 32, if any)."""
         k, v = self.k_cache, self.v_cache
-        if self.layout == "bhld":
+        if self.layout == "bhld_vt":
+            B_, H_, T_, DB_, _, _, _ = v.shape
+            v = v.permute(0, 1, 2, 4, 6, 3, 5).reshape(B_, H_, T_, 32, DB_ * 16)             # [.., pos, D]
+            v = v[:, :, :, VT_POS_OF, :].reshape(B_, H_, T_ * 32, DB_ * 16)
+        if self.layout in ("bhld", "bhld_vt"):
             k, v = k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)
+        if not full:
+            k, v = k[:, :self.lmax_gen], v[:, :self.lmax_gen]
         return to_host_bits(k.contiguous()), to_host_bits(v.contiguous())
 
     # -- the four entry points

@@ -249,3 +249,26 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define SPEC_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and (int(m.group(1)) << int(m.group(2))) == bd.SPEC_NOALLOC_SCRATCH_BYTES
+
+
+def test_v_layout_validation():
+    hm = dict(lmax=4160, strides=(8 * 4160 * 128, 128, 4160 * 128))
+    ok_desc = good_desc(**hm)
+    ok_desc.v_layout = bd.SPEC_V_TILE32
+    assert bd.spec_verify_attn_workspace(ok_desc) > 0             # valid (two requests: split)
+    cases = [
+        (dict(**hm), 7, bd.SPEC_EINVAL, "v_layout"),                              # not a layout
+        (dict(dtype=bd.SPEC_F32, **hm), bd.SPEC_V_TILE32, bd.SPEC_EUNSUPPORTED, "bf16"),
+        (dict(), bd.SPEC_V_TILE32, bd.SPEC_EINVAL, "head-major"),                 # token-major strides
+        (dict(lmax=4156, strides=(8 * 4156 * 128, 128, 4156 * 128)), bd.SPEC_V_TILE32, bd.SPEC_EINVAL, "lmax"),
+    ]
+    for kw, vl, status, word in cases:
+        desc = good_desc(**kw)
+        desc.v_layout = vl
+        assert bd.spec_verify_attn_workspace(desc) == 0
+        with pytest.raises(bd.SpecError) as e:
+            attn(desc)
+        assert e.value.status == status and word in str(e.value), (kw, vl, str(e.value))
+        with pytest.raises(bd.SpecError) as e:
+            bd.spec_commit_kv(desc, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, stream=0)
+        assert e.value.status == status

@@ -206,15 +206,17 @@ def test_main_streams_ignore_stream_rows_bitwise():
     assert not torch.equal(st.out[:, T:], base[:, T:])
 
 
-def test_msa_full_size_sampled():
+@pytest.mark.parametrize("layout", ["bhld", "bhld_vt"])
+def test_msa_full_size_sampled(layout):
     """The multi-stream workload at full size in the benchmark's launch configuration
-    (head-major cache, automatic split); attention on sampled rows (main and stream rows
-    of first, middle and last nodes), everything else everywhere."""
+    (head-major cache with V in transposed 32-key tiles, automatic split; row-major V
+    too); attention on sampled rows (main and stream rows of first, middle and last
+    nodes), everything else everywhere."""
     cfg = wl.CONFIGS["c6_msa_1b"]
     reqs, rows = [0, 3, 7], [0, 1, 20, 39, 40, 42, 100, 159]
-    say("[gpu] full-size c6_msa_1b: generate")
+    say(f"[gpu] full-size c6_msa_1b {layout}: generate")
     x = wl.generate(cfg)
-    st = VerifyStep(cfg, x, layout="bhld")
+    st = VerifyStep(cfg, x, layout=layout)
     say(f"[gpu] full-size c6_msa_1b: run step (ws {st.ws_bytes} B)")
     st.run()
     torch.cuda.synchronize()
@@ -233,9 +235,10 @@ def test_msa_full_size_sampled():
     np.testing.assert_array_equal(st.out_bonus.cpu().numpy(), bonus)
     L = x["cache_len"]
     np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L + A)
-    k_host, _ = st.cache_host()
+    k_host, v_host = st.cache_host()
     for b in range(cfg.B):
         for d in range(int(A[b])):
             np.testing.assert_array_equal(k_host[b, L[b] + d], x["k_blk"][b, path[b, d]])
+            np.testing.assert_array_equal(v_host[b, L[b] + d], x["v_blk"][b, path[b, d]])
     check_next_draft(st, x, cfg, A, path, bonus)
     say(f"    accepted lengths {A.tolist()}")

@@ -106,6 +106,25 @@ def test_mask_and_attention_small(case):
     compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
 
 
+BF16_SMALL = [c for c in SMALL_CASES if wl.CONFIGS[c[1]].dtype == "bf16"]
+
+
+@pytest.mark.parametrize("case", BF16_SMALL, ids=[c[0] for c in BF16_SMALL])
+def test_attention_small_transposed_v(case):
+    # V in transposed 32-key tiles (SPEC_V_TILE32): ragged last tiles whose unused
+    # slots hold NaN, split boundaries, empty prefixes, ragged block rows
+    cid, name, over, splits = case
+    cfg = wl.CONFIGS[name]
+    x = wl.generate(cfg, **over, with_logits=False)
+    st = VerifyStep(cfg, x, kv_splits=splits, layout="bhld_vt")
+    say(f"[gpu] {cid} (transposed V): build_mask + attention (ws {st.ws_bytes} B)")
+    st.build_mask()
+    st.attention()
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_attention(x, cfg)
+    compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
+
+
 def test_mid_size_block_two_group_kernel():
     # 15 nodes + 15 contemplate rows, GQA group 4: 120 rows per kv-head, the
     # largest block that still runs two wave groups of 64-row slices
@@ -119,14 +138,15 @@ def test_mid_size_block_two_group_kernel():
     compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
 
 
-def test_large_scores_rescale_often():
+@pytest.mark.parametrize("layout", ["blhd", "bhld_vt"])
+def test_large_scores_rescale_often(layout):
     # queries scaled by 6: scores spread over tens of log2 units, so the running
     # max moves by more than the rescale threshold inside the steady-state steps
     cfg = wl.CONFIGS["c3_confu_8b"].with_(name="c3_q6")
     x = wl.generate(cfg, B=1, L=(2047, 2047), with_logits=False)
     qf = (x["q"].astype(np.uint32) << 16).view(np.float32) * np.float32(6.0)
     x["q"] = wl.f32_to_bf16_bits(qf)
-    st = VerifyStep(cfg, x)
+    st = VerifyStep(cfg, x, layout=layout)
     st.build_mask()
     st.attention()
     torch.cuda.synchronize()
@@ -148,10 +168,11 @@ def wl_values(a, cfg):
     return v[np.isfinite(v)]
 
 
-def test_d64_bf16_mfma_path():
+@pytest.mark.parametrize("layout", ["blhd", "bhld_vt"])
+def test_d64_bf16_mfma_path(layout):
     cfg = wl.CONFIGS["c3_confu_8b"].with_(D=64, name="c3_d64")
     x = wl.generate(cfg, B=2, L=(130, 161), with_logits=False)
-    st = VerifyStep(cfg, x)
+    st = VerifyStep(cfg, x, layout=layout)
     st.build_mask()
     st.attention()
     torch.cuda.synchronize()
@@ -159,11 +180,12 @@ def test_d64_bf16_mfma_path():
     compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
 
 
-def test_max_block_rows():
+@pytest.mark.parametrize("layout", ["blhd", "bhld_vt"])
+def test_max_block_rows(layout):
     # Tq = 256 block rows (the limit), 64 chains of 4, GQA group 2
     cfg = wl.CONFIGS["c5_stream_70b"].with_(Hq=4, Hkv=2, T=256, chain_len=4, name="c5_tq256")
     x = wl.generate(cfg, B=1, L=(40, 40), with_logits=False)
-    st = VerifyStep(cfg, x)
+    st = VerifyStep(cfg, x, layout=layout)
     st.build_mask()
     st.attention()
     torch.cuda.synchronize()
@@ -184,10 +206,11 @@ def test_single_row_block():
     compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
 
 
-def test_invisible_keys_do_not_change_outputs_bitwise():
+@pytest.mark.parametrize("layout", ["blhd", "bhld_vt"])
+def test_invisible_keys_do_not_change_outputs_bitwise(layout):
     cfg = wl.CONFIGS["c3_confu_8b"]
     x = wl.generate(cfg, B=2, L=(200, 200), with_logits=False)
-    st = VerifyStep(cfg, x)
+    st = VerifyStep(cfg, x, layout=layout)
     st.build_mask()
     st.attention()
     base = st.out.clone()
@@ -198,22 +221,33 @@ def test_invisible_keys_do_not_change_outputs_bitwise():
     st.v_blk[:, T:] = torch.randn(st.v_blk[:, T:].shape, generator=g, device="cuda").to(torch.bfloat16)
     st.k_soft.copy_(torch.randn(st.k_soft.shape, generator=g, device="cuda").to(torch.bfloat16))
     st.v_soft.copy_(torch.randn(st.v_soft.shape, generator=g, device="cuda").to(torch.bfloat16))
-    # cache slots past the prefix: garbage of another kind
-    st.k_cache[:, 200:] = 1e4
+    # cache slots past the prefix: garbage of another kind (infinities in the V tile
+    # that holds the prefix's last keys when V is tiled)
+    if layout == "blhd":
+        st.k_cache[:, 200:] = 1e4
+        st.v_cache[:, 200:] = float("inf")
+    else:
+        from masked_verification_attention_amd.step import VT_POS_OF
+        st.k_cache[:, :, 200:] = 1e4
+        for k in range(200 % 32, 32):                     # tile [D/16][group][16][slot]
+            g, e = divmod(VT_POS_OF[k], 8)
+            st.v_cache[:, :, 200 // 32, :, g, :, e] = float("inf")
+        st.v_cache[:, :, 200 // 32 + 1:] = 1e4
     st.attention()
     torch.cuda.synchronize()
     assert torch.equal(st.out[:, :T], base[:, :T])
     assert not torch.equal(st.out[:, T:], base[:, T:])
 
 
+@pytest.mark.parametrize("layout", ["blhd", "bhld_vt"])
 @pytest.mark.parametrize("name", ["c3_confu_8b", "c4_tree_3b"])
-def test_truncated_block_leaves_earlier_rows_bitwise(name):
+def test_truncated_block_leaves_earlier_rows_bitwise(name, layout):
     """Parents precede children, so cutting a request's block after row n' leaves
     what rows < n' see unchanged; their outputs must not move by a single bit
     although the rows sharing their waves and the block's tile count change."""
     cfg = wl.CONFIGS[name]
     x = wl.generate(cfg, B=3, L=(300, 500), with_logits=False)
-    st = VerifyStep(cfg, x)
+    st = VerifyStep(cfg, x, layout=layout)
     st.build_mask()
     st.attention()
     torch.cuda.synchronize()
@@ -334,18 +368,23 @@ def test_full_step_chain_matches_oracle():
     np.testing.assert_array_equal(st.out_path.cpu().numpy(), path)
 
 
-@pytest.mark.parametrize("name", ["c1_tiny_la", "c2_la_7b", "c3_confu_8b", "c4_tree_3b", "c5_stream_70b"])
-def test_head_major_cache_layout(name):
-    # the cache may be [B, Hkv, lmax, D] (head-major) through the descriptor's strides
+HEAD_MAJOR = [(n, "bhld") for n in ["c1_tiny_la", "c2_la_7b", "c3_confu_8b", "c4_tree_3b", "c5_stream_70b"]] + \
+    [(n, "bhld_vt") for n in ["c2_la_7b", "c3_confu_8b", "c4_tree_3b", "c5_stream_70b"]]
+
+
+@pytest.mark.parametrize("name,layout", HEAD_MAJOR, ids=[f"{n}-{l}" for n, l in HEAD_MAJOR])
+def test_head_major_cache_layout(name, layout):
+    # the cache may be [B, Hkv, lmax, D] (head-major) through the descriptor's strides, with V
+    # row-major or in transposed 32-key tiles; the whole step, commit included
     cfg = wl.CONFIGS[name]
     x = wl.generate(cfg, B=min(cfg.B, 2), L=(70, 140) if cfg.L[0] else None)
-    st = VerifyStep(cfg, x, layout="bhld")
+    st = VerifyStep(cfg, x, layout=layout)
     st.run()
     torch.cuda.synchronize()
     ref, ref_lse = oracle_attention(x, cfg)
     compare_attention(st.out.cpu().numpy(), st.lse.cpu().numpy(), ref, ref_lse, cfg, x)
-    greedy, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
-                                           x["acc_parent"], st.max_depth)
+    _, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                      x["acc_parent"], st.max_depth)
     kc, vc, L2 = oracle.commit_kv(x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"], x["v_blk"], A, path)
     np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L2)
     k_host, v_host = st.cache_host()
@@ -362,16 +401,20 @@ FULL_SAMPLES = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(FULL_SAMPLES))
-def test_full_size_sampled(name):
+FULL_CASES = [(n, "bhld_vt") for n in sorted(FULL_SAMPLES)] + [("c3_confu_8b", "bhld")]
+
+
+@pytest.mark.parametrize("name,layout", FULL_CASES, ids=[f"{n}-{l}" for n, l in FULL_CASES])
+def test_full_size_sampled(name, layout):
     """Whole workload at its full size in the benchmark's launch configuration
-    (automatic split, head-major cache); attention checked on sampled rows, the
+    (automatic split, head-major cache, V in transposed 32-key tiles; row-major V
+    too for the headline workload); attention checked on sampled rows, the
     argmax / acceptance / commit checked everywhere."""
     cfg = wl.CONFIGS[name]
     reqs, rows = FULL_SAMPLES[name]
-    say(f"[gpu] full-size {name}: generate")
+    say(f"[gpu] full-size {name} {layout}: generate")
     x = wl.generate(cfg)
-    st = VerifyStep(cfg, x, layout="bhld")
+    st = VerifyStep(cfg, x, layout=layout)
     say(f"[gpu] full-size {name}: run step (ws {st.ws_bytes} B)")
     st.run()
     torch.cuda.synchronize()
@@ -433,6 +476,42 @@ def test_fused_accept_commit_matches_oracle(name):
     kc, vc, L2 = oracle.commit_kv(x["k_cache"], x["v_cache"], L0, x["k_blk"], x["v_blk"], A, path)
     np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L2)
     k_host, v_host = st.cache_host()
+    np.testing.assert_array_equal(k_host, kc)
+    np.testing.assert_array_equal(v_host, vc)
+    say(f"    accepted {A.tolist()}, new lengths {L2.tolist()}")
+
+
+def _padded_cache(a, lmax):
+    """A generator cache [B, lmax0, Hkv, D] widened to lmax slots of NaN canaries."""
+    pad = lmax - a.shape[1]
+    if pad == 0:
+        return a
+    fill = np.full((a.shape[0], pad) + a.shape[2:], 0x7FC0 if a.dtype == np.uint16 else np.nan, dtype=a.dtype)
+    return np.concatenate([a, fill], axis=1)
+
+
+@pytest.mark.parametrize("name", ["c2_la_7b", "c3_confu_8b", "c4_tree_3b", "c5_stream_70b", "c6_msa_1b"])
+def test_fused_accept_commit_transposed_v(name):
+    # the fused commit writes accepted V rows into transposed 32-key tiles, capacity rule included
+    cfg = wl.CONFIGS[name]
+    say(f"[gpu] fused accept+commit {name}, transposed V")
+    x = wl.generate(cfg, B=min(cfg.B, 3), L=(40, 90))
+    st = VerifyStep(cfg, x, layout="bhld_vt")
+    L0 = np.array([st.lmax - 1] + [int(v) for v in x["cache_len"][1:]], dtype=np.int32)
+    st.cache_len.copy_(torch.from_numpy(L0))
+    st.accept_commit()
+    torch.cuda.synchronize()
+    if cfg.structure == "msa_tree":
+        _, A, path, _, _ = oracle.argmax_accept_rows(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                                     x["acc_parent"], x["acc_parent"], st.max_depth)
+    else:
+        _, A, path = oracle.argmax_accept(x["logits"], cfg.logits_dtype, x["n_nodes"], x["draft_tok"],
+                                          x["acc_parent"], st.max_depth)
+    np.testing.assert_array_equal(st.out_len.cpu().numpy(), A)
+    kc, vc, L2 = oracle.commit_kv(_padded_cache(x["k_cache"], st.lmax), _padded_cache(x["v_cache"], st.lmax), L0,
+                                  x["k_blk"], x["v_blk"], A, path)
+    np.testing.assert_array_equal(st.cache_len_out.cpu().numpy(), L2)
+    k_host, v_host = st.cache_host(full=True)
     np.testing.assert_array_equal(k_host, kc)
     np.testing.assert_array_equal(v_host, vc)
     say(f"    accepted {A.tolist()}, new lengths {L2.tolist()}")

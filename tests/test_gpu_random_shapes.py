@@ -57,7 +57,9 @@ def draw_case(i):
     if cfg.Tq > 256:
         cfg = cfg.with_(T=max(1, 256 // (1 + cfg.gamma)) if structure == "msa_tree" else 256)
     B = int(rng.integers(1, 4))
-    layout = str(rng.choice(["blhd", "bhld"]))
+    layout = str(rng.choice(["blhd", "bhld", "bhld_vt"]))
+    if layout == "bhld_vt" and cfg.dtype != "bf16":
+        layout = "bhld"                                  # transposed V tiles are a bf16 layout
     splits = int(rng.choice([0, 0, 2, 5]))
     V = int(rng.choice([1003, 4096, 32000]))
     cfg = cfg.with_(V=V)
