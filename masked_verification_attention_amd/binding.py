@@ -139,6 +139,36 @@ def _check(status: int, func: str):
         raise SpecError(status, func, load().spec_last_error().decode())
 
 
+class Prepared:
+    """One entry-point call with its arguments converted once (device addresses,
+    descriptor reference, stream handle): calling it only crosses the C ABI.  For
+    loops that launch the same calls many times, where converting arguments per
+    call would cost more host time than the kernels take on the device."""
+
+    __slots__ = ("name", "fn", "args", "keep")
+
+    def __init__(self, name: str, *args, stream=None):
+        lib = load()
+        self.name = name
+        self.fn = getattr(lib, name)
+        self.keep = args                       # keeps tensors and descriptors alive
+        conv = []
+        for a in args:
+            if isinstance(a, AttnDesc):
+                conv.append(ctypes.byref(a))
+            elif a is None or isinstance(a, (int, float)):
+                conv.append(a)
+            else:
+                conv.append(_ptr(a))
+        conv.append(_stream(stream))
+        self.args = tuple(conv)
+
+    def __call__(self):
+        status = self.fn(*self.args)
+        if status != SPEC_OK:
+            _check(status, self.name)
+
+
 def make_desc(B, Tq, Hq, Hkv, D, S, dtype, lmax, strides, scale=0.0, kv_splits=0, v_layout=SPEC_V_ROWS) -> AttnDesc:
     sb, sl, sh = strides
     return AttnDesc(B, Tq, Hq, Hkv, D, S, dtype, scale, lmax, sb, sl, sh, kv_splits, v_layout)

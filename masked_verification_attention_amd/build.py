@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
+# measured-ceiling probes the benchmark reports beside the published peaks (not the library's ABI)
+PROBE_SRC = os.path.join(PKG, "probes", "ceilings.hip")
+PROBE_LIB = os.path.join(PKG, "probes", "libspecprobe.so")
 
 SOURCES = ["api.hip", "mask.hip", "attn_valu.hip", "attn_mfma.hip", "accept.hip", "commit.hip", "draft.hip"]
 ARCH = os.environ.get("SPEC_OFFLOAD_ARCH", "gfx950")
@@ -52,10 +55,23 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_probes() -> str:
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, PROBE_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed on the probes:\n{errs}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 6)) as ex:
+        probes = ex.submit(build_probes)
         objs = list(ex.map(_compile, SOURCES))
+        probes.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -226,11 +226,9 @@ class VerifyStep:
                            self.out_len, self.out_path, self.max_depth, self.out_bonus, self.cfg.gamma,
                            self.cfg.branch, self.next_topk, self.next_tok, self.next_parent, self.next_n, stream)
 
-    def run(self, stream=None):
-        """One pass of the whole hot path (the cache length is not advanced in place);
-        multi-stream workloads also draft the next tree in the same pass."""
-        self.build_mask(stream)
-        self.attention(stream)
+    def tail(self, stream=None):
+        """Everything after the attention: greedy tokens, acceptance and commit (and the
+        next draft of multi-stream workloads)."""
         if self.accept == "greedy":
             self.accept_commit(stream)
         else:
@@ -238,3 +236,43 @@ class VerifyStep:
             self.commit(stream)
         if self.msa:
             self.draft(stream)
+
+    def run(self, stream=None):
+        """One pass of the whole hot path (the cache length is not advanced in place);
+        multi-stream workloads also draft the next tree in the same pass."""
+        self.build_mask(stream)
+        self.attention(stream)
+        self.tail(stream)
+
+    def prepare(self, stream=None):
+        """The calls of run() with their arguments converted once, as three lists of
+        zero-argument callables (mask, attention, tail) on ``stream``."""
+        P = bd.Prepared
+        dt = DTYPE_CODE[self.cfg.logits_dtype]
+        if self.msa:
+            mask = [P("spec_build_msa_mask", self.tree_parent, self.n_nodes, self.B, self.tree_parent.shape[1],
+                      self.cfg.gamma, self.Tq, self.mask_bits, self.sp_bits, self.n_q, stream=stream)]
+        else:
+            mask = [P("spec_build_mask", self.attn_parent, self.sp_flag, self.n_q, self.B, self.Tq, self.mask_bits,
+                      self.sp_bits, stream=stream)]
+        attn = [P("spec_verify_attn", self.desc, self.q, self.k_cache, self.v_cache, self.cache_len, self.k_blk,
+                  self.v_blk, self.k_soft, self.v_soft, self.mask_bits, self.sp_bits, self.n_q, self.out, self.lse,
+                  self.workspace, int(self.ws_bytes), stream=stream)]
+        vrow = self.acc_parent if self.msa else None
+        if self.accept == "greedy":
+            tail = [P("spec_argmax_accept_commit", self.logits, dt, self.T, self.V, self.n_nodes, self.draft_tok,
+                      self.acc_parent, vrow, self.max_depth, self.argmax, self.out_len, self.out_path,
+                      self.out_bonus, self.desc, self.k_cache, self.v_cache, self.cache_len, self.cache_len_out,
+                      self.k_blk, self.v_blk, stream=stream)]
+        else:
+            mode = bd.SPEC_ACCEPT_THRESHOLD if self.accept == "threshold" else bd.SPEC_ACCEPT_SOFT
+            tail = [P("spec_prob_accept", self.logits, dt, self.B, self.T, self.V, self.n_nodes, self.draft_tok,
+                      self.acc_parent, vrow, self.max_depth, mode, self.threshold, self.draft_prob, self.uniform,
+                      self.argmax, self.out_prob, self.out_len, self.out_path, self.out_bonus, stream=stream),
+                    P("spec_commit_kv", self.desc, self.k_cache, self.v_cache, self.cache_len, self.cache_len_out,
+                      self.k_blk, self.v_blk, self.out_len, self.out_path, self.max_depth, stream=stream)]
+        if self.msa:
+            tail.append(P("spec_draft_tree", self.logits, dt, self.B, self.Tq, self.V, self.n_nodes, self.out_len,
+                          self.out_path, self.max_depth, self.out_bonus, self.cfg.gamma, self.cfg.branch,
+                          self.next_topk, self.next_tok, self.next_parent, self.next_n, stream=stream))
+        return mask, attn, tail

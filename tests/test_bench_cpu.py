@@ -61,12 +61,37 @@ def test_counter_summary_scales_by_the_copy(tmp_path):
         for r in rows:
             w.writerow(r)
     out = tmp_path / "rec.json"
-    old = bench.COUNTERS_FILE
-    bench.COUNTERS_FILE = str(out)
-    try:
-        bench.summarize_pmc(str(d))
-    finally:
-        bench.COUNTERS_FILE = old
+    bench.summarize_pmc(str(d), "c3_confu_8b", out=str(out))
     rec = json.load(open(out))
+    assert rec["workload"] == "c3_confu_8b" and len(rec["kernel_src_sha256"]) == 64 and rec["taken"]
     assert abs(rec["fetch_scale"] - 2.0) < 1e-12 and abs(rec["write_scale"] - 1.0) < 1e-12
     assert abs(rec["traffic_bytes_per_launch"] - (1000 * 1024 * 2 + 100 * 1024)) < 1e-6
+
+
+def test_counter_record_is_keyed_on_workload_and_kernel_source(tmp_path, monkeypatch):
+    rec = {"workload": "c4_tree_3b", "kernel_src_sha256": "0" * 64, "traffic_bytes_per_launch": 1.0, "taken": "x"}
+    path = tmp_path / "attn_mfma_c4_tree_3b_counters.json"
+    path.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "counters_file", lambda w: str(tmp_path / f"attn_mfma_{w}_counters.json"))
+    assert bench.counters_traffic("c4_tree_3b") == (None, None)          # stale source hash
+    import hashlib
+    rec["kernel_src_sha256"] = hashlib.sha256(open(bench.ATTN_SRC, "rb").read()).hexdigest()
+    path.write_text(json.dumps(rec))
+    traffic, src = bench.counters_traffic("c4_tree_3b")
+    assert traffic == 1.0 and src["kernel_src_sha256"] == rec["kernel_src_sha256"] and src["taken"] == "x"
+    assert bench.counters_traffic("c3_confu_8b") == (None, None)         # no record for that workload
+
+
+def test_argmax_bytes_count_node_rows():
+    cfg = wl.CONFIGS["c6_msa_1b"]
+    x = wl.generate(cfg, B=2)
+    assert bench.argmax_bytes(cfg, x) == int(x["n_nodes"].sum()) * cfg.V * 2
+    c1 = wl.CONFIGS["c1_tiny_la"]
+    x1 = wl.generate(c1)
+    assert bench.argmax_bytes(c1, x1) == 4 * 1000 * 4
+
+
+def test_every_workload_has_a_description_and_bound():
+    for name in ["c1_tiny_la", "c2_la_7b", "c3_confu_8b", "c4_tree_3b", "c5_stream_70b", "c6_msa_1b"]:
+        desc, seq_len, bound = bench.DESCRIPTIONS[name]
+        assert name in wl.CONFIGS and seq_len > 0 and bound in ("hbm", "mfma", "latency")

@@ -85,3 +85,34 @@ def test_concurrent_streams_match_serial():
             for a, b in zip((s.out, s.lse, s.argmax, s.out_len, s.out_path, s.cache_len_out), r):
                 assert torch.equal(a, b), rep
     say("[gpu] two streams: 5 concurrent rounds match the serial results")
+
+
+@pytest.mark.parametrize("name,accept", [("c3_confu_8b", "greedy"), ("c3_confu_8b", "soft"),
+                                         ("c6_msa_1b", "greedy")])
+def test_prepared_calls_match_regular_calls(name, accept):
+    # the benchmark's launch path (arguments converted once) against the regular binding calls
+    import numpy as np
+    cfg = wl.CONFIGS[name]
+    x = wl.generate(cfg, B=2, seed=cfg.seed + 3)
+    rng = np.random.default_rng(1)
+    T = x["acc_parent"].shape[1]
+    kw = dict(layout="bhld", accept=accept, threshold=1e-3,
+              draft_prob=(rng.random((2, T)) * 0.02).astype(np.float32),
+              uniform=rng.random((2, T)).astype(np.float32))
+    a, b = VerifyStep(cfg, x, **kw), VerifyStep(cfg, x, **kw)
+    a.run()
+    stream = torch.cuda.current_stream()
+    for calls in b.prepare(stream):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    names = ["out", "lse", "argmax", "out_len", "out_path", "cache_len_out", "mask_bits", "sp_bits"]
+    if a.msa:
+        names += ["out_bonus", "next_tok", "next_parent", "next_n"]
+    if accept != "greedy":
+        names += ["out_prob"]
+    for n in names:
+        assert torch.equal(getattr(a, n), getattr(b, n)), n
+    ka, va = a.cache_host()
+    kb, vb = b.cache_host()
+    assert (ka == kb).all() and (va == vb).all()
