@@ -76,6 +76,17 @@ __device__ __forceinline__ void dma16(uint32_t lds, const char* src) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// 4-byte direct-to-LDS load: lane i's word lands at LDS byte address lds + 4 i.
+__device__ __forceinline__ void dma4(uint32_t lds, const void* src) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// Wait until every LDS read (and scalar load) of this wave has returned.
+__device__ __forceinline__ void wait_lgkm0() {
+  // vmcnt and expcnt at their maxima (unconstrained), lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();

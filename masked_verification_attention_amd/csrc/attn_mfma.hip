@@ -70,7 +70,8 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   constexpr int DC = D / 32;   // k-chunks of S^T = K Q^T
   constexpr int DB = D / 16;   // 16-wide head-dim blocks of O^T
   __shared__ __attribute__((aligned(1024))) char ring[(C::NSK + C::NSV) * C::TILEB];
-  __shared__ uint32_t mask_lds[C::ROWS][C::MAXW];
+  __shared__ uint32_t mask_lds[C::ROWS * C::MAXW];   // row rl's word w at rl * W + w
+  __shared__ uint32_t sp_lds[64];                      // the request's soft-prompt words
 
   // ---- which (split, request, kv-head, row chunk): siblings of a row chunk
   // sit on the same XCD (workgroups are dealt round-robin over 8 XCDs)
@@ -188,21 +189,47 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     for (int j = 0; j < C::LPS; ++j) issue_one(r, j);
   };
 
-  // The first steps' tiles go out before the setup loads below, so their HBM
-  // latency overlaps that of the queries and mask words instead of following it.
+  // ---- setup loads.  Everything a wave needs before the first step comes
+  // through the same direct-to-LDS path as the tiles, ahead of them, so that
+  // no compiler-generated wait (which would count the tile loads too) stands
+  // between the setup and the first step: the workgroup's query rows (staged
+  // in V slots 4..7, which the tile stream first writes at step P/2), the mask
+  // words of its rows and the request's soft-prompt words.  Rows past the end
+  // or past the request's queries read an in-range row; the values are not used.
+  const int row0 = chunk_id * C::ROWS;
+  constexpr int QOPS = C::ROWS * D * 2 / 1024 / C::kWaves;   // 1 KB query loads per wave
+  static_assert(QOPS >= 1 && QOPS * 1024 * C::kWaves == C::ROWS * D * 2, "query staging split");
+  static_assert(C::ROWS * D * 2 <= 4 * C::TILEB, "query rows fit in V slots 4..7");
+  const char* const qstage = ring + (C::NSK + 4) * C::TILEB;
+  {
+    // 16-byte chunk c of stage row rr sits at position c ^ (rr mod CH)
+#pragma unroll
+    for (int jq = 0; jq < QOPS; ++jq) {
+      const int n = (wave * QOPS + jq) * 64 + lane;
+      const int rr = n / C::CH, c = (n % C::CH) ^ (rr & (C::CH - 1));
+      const int m = row0 + rr;
+      const int r = min(m / a.G, a.Tq - 1), g = m % a.G;
+      dma16(ring_lds + (C::NSK + 4) * C::TILEB + (wave * QOPS + jq) * 1024,
+            static_cast<const char*>(a.q) + ((((int64_t)b * a.Tq + r) * a.Hq + h * a.G + g) * D + 8 * c) * 2);
+    }
+    const uint32_t mask_addr = (uint32_t)(uintptr_t)(lds_char*)(char*)mask_lds;
+    const int nmw = C::ROWS * a.W / 64;   // ROWS is a multiple of 64: whole wave loads
+    for (int k = wave; k < nmw; k += C::kWaves) {
+      const int n = k * 64 + lane;
+      const int r = min((row0 + n / a.W) / a.G, a.Tq - 1);
+      dma4(mask_addr + k * 256, a.mask_bits + ((int64_t)b * a.Tq + r) * a.W + n % a.W);
+    }
+    if (a.S > 0 && wave == C::kWaves - 1)
+      dma4((uint32_t)(uintptr_t)(lds_char*)(char*)sp_lds, a.sp_bits + (int64_t)b * a.W + min(lane, a.W - 1));
+  }
+
+  // The first steps' tiles follow; their HBM latency overlaps the setup's.
   if (nt > 0) {
 #pragma unroll
     for (int u = 0; u < C::P / 2; ++u) issue_step(u);
   }
 
-  // ---- rows: mask words of the workgroup's rows into LDS; this lane's rows
-  const int row0 = chunk_id * C::ROWS;
-  for (int i = tid; i < C::ROWS * a.W; i += C::kThreads) {
-    const int rl = i / a.W, w = i % a.W;
-    const int m = row0 + rl;
-    const int r = m / a.G;
-    mask_lds[rl][w] = (m < a.R && r < nq) ? a.mask_bits[((int64_t)b * a.Tq + r) * a.W + w] : 0u;
-  }
+  // ---- this lane's rows
   int row_r[NB], row_j[NB], row_l[NB];
   bool row_ok[NB], row_sp[NB];
   bf16x8 qf[NB][DC];
@@ -214,15 +241,6 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     row_r[nb] = r;
     row_j[nb] = h * a.G + g;
     row_ok[nb] = (m < a.R) && (r < nq);
-    row_sp[nb] = row_ok[nb] && a.S > 0 && ((a.sp_bits[(int64_t)b * a.W + (r >> 5)] >> (r & 31)) & 1u);
-    const char* qp = static_cast<const char*>(a.q) +
-                     ((((int64_t)b * a.Tq + r) * a.Hq + row_j[nb]) * D + 8 * q4) * 2;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok[nb]) v = ldg16(qp + dc * 64);
-      qf[nb][dc] = as_bf16x8(v);
-    }
   }
 
   float mrun[NB], lrun[NB], negm[NB];
@@ -237,10 +255,32 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   }
   const int lx16 = ((lane ^ 16) << 2), lx32 = ((lane ^ 32) << 2);   // byte lane addresses for permutes
 
-  // setup loads (queries, flags, mask words) must land before the ring's vmcnt
-  // accounting starts; the first steps' tiles, issued before them, land with them
-  __builtin_amdgcn_s_waitcnt(0);
+  // The wave's setup loads have landed once no more than its tile loads are in
+  // flight (K loaders issued P/2 steps of them, V loaders P/2 - 1: their first
+  // step has no tile); after the barrier every wave's have.
+  if (nt == 0)
+    wait_vmcnt<0>();
+  else if (load_v)
+    wait_vmcnt<(C::P / 2 - 1) * C::LPS>();
+  else
+    wait_vmcnt<(C::P / 2) * C::LPS>();
   block_barrier();
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int rr = row_l[nb];
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const int pos = (4 * dc + q4) ^ (rr & (C::CH - 1));
+      u32x4 v = *reinterpret_cast<const u32x4*>(qstage + rr * C::ROWB + pos * 16);
+      if (!row_ok[nb]) v = u32x4{0u, 0u, 0u, 0u};
+      qf[nb][dc] = as_bf16x8(v);
+    }
+    const int r = row_r[nb];
+    row_sp[nb] = row_ok[nb] && a.S > 0 && ((sp_lds[min(r, a.Tq - 1) >> 5] >> (r & 31)) & 1u);
+  }
+  // the staged queries are overwritten by step P/2's V loads, issued only after
+  // a barrier that every wave reaches after this
+  wait_lgkm0();
 
   const float P_LIMIT = 256.0f;   // 2^TAU with TAU = 8: bound on any probability between rescales
   if (nt > 0) {
@@ -395,7 +435,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         need[nb] = (check_empty && mrun[nb] == -INFINITY) || !(ps[nb] <= P_LIMIT);
         any_need = any_need || need[nb];
       }
-      if (__any(any_need)) {
+      if (__builtin_expect(__any(any_need), 0)) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) rescale(nb, xs[nb], p[nb], ps[nb], need[nb]);
       }
@@ -416,7 +456,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         } else if (seg == 1) {
           vis = row_sp[nb] ? 0xffu : 0u;
         } else {
-          const uint32_t mw = mask_lds[row_l[nb]][t - ntp - nts];
+          const uint32_t mw = row_ok[nb] ? mask_lds[row_l[nb] * a.W + (t - ntp - nts)] : 0u;
           vis = ((mw >> (4 * q4)) & 0xfu) | (((mw >> (16 + 4 * q4)) & 0xfu) << 4);
         }
         // keys below lim: slots e < 4 hold keys 4 q4 + e, slots e >= 4 keys 16 + 4 q4 + e - 4
