@@ -445,23 +445,23 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         pack(nb, p[nb]);
       }
     };
-    // softmax of a tile that needs masking: ragged prefix tail, soft prompt, block rows
-    auto softmax_masked = [&](int t, int seg, int lim) __attribute__((always_inline)) {
+    // softmax of a tile that needs masking: ragged prefix tail (seg 0), soft
+    // prompt (seg 1), block rows (seg 2, whose mask words the caller read: mw)
+    auto softmax_masked = [&](int seg, int lim, const uint32_t (&mw)[NB]) __attribute__((always_inline)) {
+      // keys below lim: slots e < 4 hold keys 4 q4 + e, slots e >= 4 keys 16 + 4 q4 + e - 4
+      const int nlo = clampi(lim - 4 * q4, 0, 4), nhi = clampi(lim - 16 - 4 * q4, 0, 4);
+      const uint32_t in_tile = ((1u << nlo) - 1u) | (((1u << nhi) - 1u) << 4);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // visibility of the lane's 8 keys (tile keys 16 kb + 4 q4 + i) for its row
         uint32_t vis;
-        if (seg == 0) {
+        if (seg == 0)
           vis = row_ok[nb] ? 0xffu : 0u;
-        } else if (seg == 1) {
+        else if (seg == 1)
           vis = row_sp[nb] ? 0xffu : 0u;
-        } else {
-          const uint32_t mw = row_ok[nb] ? mask_lds[row_l[nb] * a.W + (t - ntp - nts)] : 0u;
-          vis = ((mw >> (4 * q4)) & 0xfu) | (((mw >> (16 + 4 * q4)) & 0xfu) << 4);
-        }
-        // keys below lim: slots e < 4 hold keys 4 q4 + e, slots e >= 4 keys 16 + 4 q4 + e - 4
-        const int nlo = clampi(lim - 4 * q4, 0, 4), nhi = clampi(lim - 16 - 4 * q4, 0, 4);
-        vis &= ((1u << nlo) - 1u) | (((1u << nhi) - 1u) << 4);
+        else
+          vis = ((mw[nb] >> (4 * q4)) & 0xfu) | (((mw[nb] >> (16 + 4 * q4)) & 0xfu) << 4);
+        vis &= in_tile;
         float xs[8], p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -475,16 +475,28 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         pack(nb, p);
       }
     };
-    auto softmax_any = [&](int t) __attribute__((always_inline)) {
-      const int seg = t < ntp ? 0 : (t < ntp + nts ? 1 : 2);
-      int lim;
+    // segment and in-tile key count of tile t; the block rows' mask words of the lane's rows
+    auto tile_kind = [&](int t, int& seg, int& lim) __attribute__((always_inline)) {
+      seg = t < ntp ? 0 : (t < ntp + nts ? 1 : 2);
       if (seg == 0) lim = min(C::TK, ke - (ks + t * C::TK));
       else if (seg == 1) lim = min(C::TK, a.S - (t - ntp) * C::TK);
       else lim = min(C::TK, nq - (t - ntp - nts) * C::TK);
-      if (seg == 0 && lim == C::TK)
+    };
+    auto read_mask = [&](int t, int seg, uint32_t (&mw)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        mw[nb] = (seg == 2 && row_ok[nb]) ? mask_lds[row_l[nb] * a.W + (t - ntp - nts)] : 0u;
+    };
+    auto softmax_any = [&](int t) __attribute__((always_inline)) {
+      int seg, lim;
+      tile_kind(t, seg, lim);
+      if (seg == 0 && lim == C::TK) {
         softmax_full(true);
-      else
-        softmax_masked(t, seg, lim);
+      } else {
+        uint32_t mw[NB];
+        read_mask(t, seg, mw);
+        softmax_masked(seg, lim, mw);
+      }
     };
     // Step s of a group: its matrix half (scores of its tile 2s+g, P*V of its
     // tile 2s+g-2), a barrier, its softmax half (of tile 2s+g).  Every wave runs
@@ -580,12 +592,72 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
     };
+    // A step after the hot ones (its own tile, if any, is a ragged prefix, soft
+    // or block tile; its P*V tile may be too).  The hot step's schedule for the
+    // scores -- K fragments first, the hand-off barrier after 12 matrix
+    // instructions -- with the V fragments read only once the K fragments are
+    // dead (both at once would overflow the registers here), then P*V and the
+    // masked softmax.
+    auto tail_step = [&](int s) __attribute__((always_inline)) {
+      begin_step(s);
+      const TileSrc src = tile_src(s + C::P / 2);
+      const int t = 2 * s + grp, tp = t - 2;   // s >= 1: tp >= 0
+      const bool has_t = t < nt, has_p = tp < nt;
+      auto read_pv = [&](bf16x8 (&vf)[DB]) __attribute__((always_inline)) {
+        if (VT && tp < ntp) {
+          read_vt(tp, vf);
+          const int plim = ke - (ks + tp * C::TK);
+          if (plim < C::TK) clip_vt(vf, plim);
+        } else {
+          read_v(tp, vf);
+        }
+      };
+      if (has_t) {   // then has_p as well
+        int seg, lim;
+        tile_kind(t, seg, lim);
+        {
+          bf16x8 kf[2][DC];
+          read_k(t, kf);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
+          scores(kf, st);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          bf16x8 vf[DB];
+          read_pv(vf);
+          pv(vf);
+        }
+        __builtin_amdgcn_s_setprio(1);
+        if (seg == 0 && lim == C::TK) {
+          softmax_full(true);
+        } else {
+          uint32_t mw[NB];
+          read_mask(t, seg, mw);
+          softmax_masked(seg, lim, mw);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
+        if (has_p) {
+          bf16x8 vf[DB];
+          read_pv(vf);
+          pv(vf);
+        }
+        block_barrier();
+      }
+    };
     const int nfull = (ke - ks) / C::TK;
     const int s_hot_end = (nfull - grp + 1) / 2;   // steps whose own tile is a full prefix tile
     if (grp == 1) block_barrier();
     generic_step(0);
     for (int s = 1; s < s_hot_end; ++s) hot_step(s);
-    for (int s = max(1, s_hot_end); s <= nsteps; ++s) generic_step(s);
+    for (int s = max(1, s_hot_end); s <= nsteps; ++s) tail_step(s);
     if (grp == 0) block_barrier();
     __builtin_amdgcn_s_waitcnt(0);
   }
