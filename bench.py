@@ -86,9 +86,10 @@ def counters_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"attn_mfma_{workload}_counters.json")
 
 
-def attention_algorithmic_bytes(cfg, x) -> int:
+def attention_algorithmic_bytes(cfg, x, fused_mask=False) -> int:
     """Bytes the attention must move at least once: KV prefix read, soft prompt,
-    queries, block K/V, mask words and the fp32 output (+ lse)."""
+    queries, block K/V, mask words (or, when the launch builds the mask itself,
+    the parent array and soft-prompt flags) and the fp32 output (+ lse)."""
     es = 2 if cfg.dtype == "bf16" else 4
     B, Tq = x["q"].shape[:2]
     W = (Tq + 31) // 32
@@ -96,7 +97,7 @@ def attention_algorithmic_bytes(cfg, x) -> int:
     soft = cfg.S * cfg.Hkv * cfg.D * 2 * es
     q = B * Tq * cfg.Hq * cfg.D * es
     blk = B * Tq * cfg.Hkv * cfg.D * 2 * es
-    mask = B * Tq * W * 4 + B * W * 4
+    mask = B * Tq * 5 if fused_mask else B * Tq * W * 4 + B * W * 4
     out = B * Tq * cfg.Hq * cfg.D * 4 + B * Tq * cfg.Hq * 4
     return kv + soft + q + blk + mask + out
 
@@ -324,6 +325,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured-ceiling probes")
     ap.add_argument("--kv-splits", type=int, default=0)
+    ap.add_argument("--mask", choices=("fused", "separate"), default="fused",
+                    help="block mask built inside the attention launch (spec_verify_attn_tree, where it "
+                         "applies: bf16, parent-array masks) or by spec_build_mask first")
     ap.add_argument("--layout", choices=("bhld", "blhd", "bhld_vt"), default="bhld")
     ap.add_argument("--instrumented-steps", type=int, default=0,
                     help="steps of the second pass with events around every call (0: max(steps, 100))")
@@ -371,13 +375,15 @@ def main():
         st = VerifyStep(cfg, x, device="cuda:0", kv_splits=args.kv_splits, layout=layout,
                         accept=args.accept, threshold=1e-3,
                         draft_prob=urng.random((cfg.B, T_acc)).astype(np.float32) * 0.02,
-                        uniform=urng.random((cfg.B, T_acc)).astype(np.float32))
+                        uniform=urng.random((cfg.B, T_acc)).astype(np.float32),
+                        fused_mask=None if args.mask == "fused" else False)
         steps_state.append((st, x))
     torch.cuda.synchronize()
     log(f"inputs: {args.sets} sets generated and uploaded in {time.time() - t0:.1f}s")
     x0 = steps_state[0][1]
     tokens_per_step = int(x0["n_q"].sum())
-    alg_bytes = attention_algorithmic_bytes(cfg, x0)
+    fused = steps_state[0][0].fused_mask
+    alg_bytes = attention_algorithmic_bytes(cfg, x0, fused_mask=fused)
     flops = attention_flops(cfg, x0)
     am_bytes = argmax_bytes(cfg, x0)
 
@@ -478,6 +484,8 @@ def main():
                                                              ceilings["mfma_bf16_tflops_32x32x16"])
     step_kernels = {
         "mask_us": stats(t_mask), "attention_us": a, "tail_us": stats(t_tail),
+        "mask": ("built inside the attention launch (spec_verify_attn_tree); mask_us is an empty interval"
+                 if fused else "spec_build_msa_mask" if cfg.structure == "msa_tree" else "spec_build_mask"),
         "tail": ("spec_argmax_accept_commit (argmax, acceptance scan + commit: two launches)"
                  if args.accept == "greedy" else "spec_prob_accept + spec_commit_kv")
                 + (" + spec_draft_tree" if cfg.structure == "msa_tree" else ""),

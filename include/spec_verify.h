@@ -15,6 +15,7 @@
  *                       [soft prompt | cached prefix | block] under that mask
  *   spec_verify_attn_noalloc  the same without a workspace argument (for
  *                       callers that cannot allocate)
+ *   spec_verify_attn_tree  mask build and attention in one launch
  *   spec_argmax_accept  per-node greedy token, longest accepted path
  *   spec_argmax_accept_rows  the same with explicit verification rows, an
  *                       explicit root and the correction token
@@ -329,6 +330,35 @@ int spec_verify_attn(const spec_attn_desc* d, const void* q,
                      const uint32_t* mask_bits, const uint32_t* sp_bits, const int32_t* n_q,
                      float* out, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * spec_verify_attn_tree -- spec_build_mask and spec_verify_attn in one launch:
+ * the attention builds each row's block mask itself from the parent array
+ * (the rule of spec_build_mask: row r < n_q[b] sees block key c iff c == r or
+ * c is an ancestor of r through parent links that point strictly upwards; the
+ * first link that does not ends the chain), so the mask never goes through
+ * memory and the step saves a kernel.  Sources: as spec_build_mask ([SS] tree
+ * draft and Equation 4, [LA] 3.1 M_LA, [CF] key design 1) and spec_verify_attn.
+ *
+ *   attn_parent [B, Tq] int32   as spec_build_mask (4-byte aligned)
+ *   sp_flag     [B, Tq] uint8   as spec_build_mask; NULL = no row sees the
+ *                               soft prompt (then S > 0 still needs k_soft
+ *                               and v_soft)
+ * Every other argument, the workspace (spec_verify_attn_workspace) and the
+ * results are those of spec_verify_attn; out and lse are bitwise equal to
+ * spec_build_mask followed by spec_verify_attn on the same inputs.
+ *
+ * bf16 inputs only (the matrix-core kernel); fp32 inputs return
+ * SPEC_EUNSUPPORTED (use the two calls).  Errors otherwise as
+ * spec_verify_attn, with attn_parent in place of mask_bits.
+ */
+int spec_verify_attn_tree(const spec_attn_desc* d, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                          const void* k_blk, const void* v_blk,
+                          const void* k_soft, const void* v_soft,
+                          const int32_t* attn_parent, const uint8_t* sp_flag, const int32_t* n_q,
+                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /*
  * spec_verify_attn_noalloc -- spec_verify_attn without a workspace argument,

@@ -316,16 +316,26 @@ size_t spec_verify_attn_workspace(const spec_attn_desc* d) {
 namespace {
 
 // Argument checks of spec_verify_attn and spec_verify_attn_noalloc (the workspace aside).
+// tree: the mask comes from a parent array (mask_bits is attn_parent, and
+// sp_bits is the optional sp_flag, so it may be NULL and needs no alignment).
 int check_attn_args(const char* fn, const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
-                    const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits, const int32_t* n_q,
-                    const float* out, const float* lse) {
+                    const void* v_soft, const void* mask_bits, const void* sp_bits, const int32_t* n_q,
+                    const float* out, const float* lse, bool tree = false) {
   const int st = check_desc(d);
   if (st != SPEC_OK) return st;
   if (d->B == 0) return SPEC_OK;
+  const char* mask_name = tree ? "attn_parent" : "mask_bits";
   REQUIRE(q && k_cache && v_cache && cache_len && k_blk && v_blk && mask_bits && n_q && out, SPEC_EINVAL,
-          "%s: q, k_cache, v_cache, cache_len, k_blk, v_blk, mask_bits, n_q and out must be non-NULL", fn);
-  if (d->S > 0) {
+          "%s: q, k_cache, v_cache, cache_len, k_blk, v_blk, %s, n_q and out must be non-NULL", fn, mask_name);
+  if (tree) {
+    if (d->S > 0) {
+      REQUIRE(k_soft && v_soft, SPEC_EINVAL, "%s: S = %d needs k_soft and v_soft", fn, d->S);
+    } else {
+      REQUIRE(!k_soft && !v_soft, SPEC_EINVAL, "%s: k_soft / v_soft given with S = 0", fn);
+    }
+    sp_bits = nullptr;   // byte flags: no alignment to check
+  } else if (d->S > 0) {
     REQUIRE(k_soft && v_soft && sp_bits, SPEC_EINVAL, "%s: S = %d needs k_soft, v_soft and sp_bits", fn, d->S);
   } else {
     REQUIRE(!k_soft && !v_soft, SPEC_EINVAL, "%s: k_soft / v_soft given with S = 0", fn);
@@ -340,10 +350,13 @@ int check_attn_args(const char* fn, const spec_attn_desc* d, const void* q, cons
 }
 
 // Enqueue a validated call; `workspace` holds at least plan.ws_bytes bytes.
+// attn_parent != NULL: the kernel builds the block mask from attn_parent /
+// sp_flag (spec_verify_attn_tree) and mask_bits / sp_bits are not read.
 int launch_verify_attn(const spec_attn_desc* d, const sv::AttnPlan& plan, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* cache_len, const void* k_blk, const void* v_blk,
                        const void* k_soft, const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
-                       const int32_t* n_q, float* out, float* lse, void* workspace, void* stream) {
+                       const int32_t* n_q, float* out, float* lse, void* workspace, void* stream,
+                       const int32_t* attn_parent = nullptr, const uint8_t* sp_flag = nullptr) {
   sv::AttnArgs a{};
   a.B = d->B;
   a.Tq = d->Tq;
@@ -377,6 +390,9 @@ int launch_verify_attn(const spec_attn_desc* d, const sv::AttnPlan& plan, const 
   a.row_chunks = plan.row_chunks;
   a.rows_per_wg = plan.rows_per_wg;
   a.v_tiled = d->v_layout == SPEC_V_TILE32;
+  a.mask_from_parent = attn_parent != nullptr;
+  a.attn_parent = attn_parent;
+  a.sp_flag = sp_flag;
   if (plan.n_split > 1) {
     const size_t rows = (size_t)plan.n_split * d->B * d->Hkv * a.R;
     char* ws = static_cast<char*>(workspace);
@@ -439,6 +455,30 @@ int spec_verify_attn(const spec_attn_desc* d, const void* q, const void* k_cache
   }
   return launch_verify_attn(d, plan, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft, mask_bits,
                             sp_bits, n_q, out, lse, workspace, stream);
+}
+
+int spec_verify_attn_tree(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
+                          const void* v_soft, const int32_t* attn_parent, const uint8_t* sp_flag,
+                          const int32_t* n_q, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  static const char* fn = "spec_verify_attn_tree";
+  const int st0 = check_desc(d);
+  if (st0 != SPEC_OK) return st0;
+  if (d->B == 0) return ok();
+  REQUIRE(d->dtype == SPEC_BF16, SPEC_EUNSUPPORTED,
+          "%s: bf16 inputs only (fp32 inputs: spec_build_mask, then spec_verify_attn)", fn);
+  const int st = check_attn_args(fn, d, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft, attn_parent,
+                                 sp_flag, n_q, out, lse, /*tree=*/true);
+  if (st != SPEC_OK) return st;
+  const sv::AttnPlan plan = sv::plan_attn(*d);
+  if (plan.ws_bytes > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, SPEC_EWORKSPACE,
+            "workspace of %zu bytes needed, %zu given", plan.ws_bytes, workspace ? workspace_bytes : 0);
+    REQUIRE(aligned(workspace, 16), SPEC_EINVAL, "workspace must be 16-byte aligned");
+  }
+  return launch_verify_attn(d, plan, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft, nullptr,
+                            nullptr, n_q, out, lse, workspace, stream, attn_parent, sp_flag);
 }
 
 int spec_verify_attn_noalloc(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,

@@ -196,6 +196,36 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   // in V slots 4..7, which the tile stream first writes at step P/2), the mask
   // words of its rows and the request's soft-prompt words.  Rows past the end
   // or past the request's queries read an in-range row; the values are not used.
+  // When the mask is built here from the parent array (mask_from_parent), the
+  // parents and soft-prompt flags come first instead, with plain loads (one per
+  // thread) consumed before any direct-to-LDS load is issued, so their waits
+  // cover nothing else; their latency overlaps that of the cache length.  The
+  // mask is then built in LDS while the queries and first tiles are in flight,
+  // in slots that the tile stream first writes at step P/2: the mask rows in
+  // K slots 6.. (8 KB), the ancestor links and flags after them.
+  const bool tree = a.mask_from_parent != 0;
+  static_assert(C::ROWS * D * 2 <= 2 * C::TILEB || D == 128, "at D = 64 the query stage leaves V slots 6, 7");
+  uint32_t* const msk_l = reinterpret_cast<uint32_t*>(ring + 6 * C::TILEB);              // [Tq][W]
+  char* const aux_l = D == 128 ? ring + 7 * C::TILEB : ring + (C::NSK + 6) * C::TILEB;
+  int32_t* const anc_l = reinterpret_cast<int32_t*>(aux_l);                              // [Tq]
+  uint8_t* const spf_l = reinterpret_cast<uint8_t*>(aux_l + SPEC_MAX_TQ * 4);              // [Tq]
+  static_assert(SPEC_MAX_TQ * ((SPEC_MAX_TQ + 31) / 32) * 4 <= 8192 && 8192 <= 2 * C::TILEB,
+                "mask rows fit in K slots 6..");
+  static_assert(SPEC_MAX_TQ * 5 <= C::TILEB, "links and flags fit in one slot");
+  static_assert(SPEC_MAX_TQ <= C::kThreads, "one parent per thread");
+  if (tree) {
+    int32_t pr = -1;
+    uint8_t f = 0;
+    if (tid < a.Tq) {
+      pr = a.attn_parent[(int64_t)b * a.Tq + tid];
+      if (a.sp_flag != nullptr) f = a.sp_flag[(int64_t)b * a.Tq + tid];
+      // row r < n_q starts as itself, linked to its parent while the link points up
+      const int r = tid;
+      anc_l[r] = (r < nq && pr >= 0 && pr < r) ? pr : -1;
+      spf_l[r] = f;
+      for (int w = 0; w < a.W; ++w) msk_l[r * a.W + w] = (r < nq && (r >> 5) == w) ? 1u << (r & 31) : 0u;
+    }
+  }
   const int row0 = chunk_id * C::ROWS;
   constexpr int QOPS = C::ROWS * D * 2 / 1024 / C::kWaves;   // 1 KB query loads per wave
   static_assert(QOPS >= 1 && QOPS * 1024 * C::kWaves == C::ROWS * D * 2, "query staging split");
@@ -212,15 +242,17 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       dma16(ring_lds + (C::NSK + 4) * C::TILEB + (wave * QOPS + jq) * 1024,
             static_cast<const char*>(a.q) + ((((int64_t)b * a.Tq + r) * a.Hq + h * a.G + g) * D + 8 * c) * 2);
     }
-    const uint32_t mask_addr = (uint32_t)(uintptr_t)(lds_char*)(char*)mask_lds;
-    const int nmw = C::ROWS * a.W / 64;   // ROWS is a multiple of 64: whole wave loads
-    for (int k = wave; k < nmw; k += C::kWaves) {
-      const int n = k * 64 + lane;
-      const int r = min((row0 + n / a.W) / a.G, a.Tq - 1);
-      dma4(mask_addr + k * 256, a.mask_bits + ((int64_t)b * a.Tq + r) * a.W + n % a.W);
+    if (!tree) {
+      const uint32_t mask_addr = (uint32_t)(uintptr_t)(lds_char*)(char*)mask_lds;
+      const int nmw = C::ROWS * a.W / 64;   // ROWS is a multiple of 64: whole wave loads
+      for (int k = wave; k < nmw; k += C::kWaves) {
+        const int n = k * 64 + lane;
+        const int r = min((row0 + n / a.W) / a.G, a.Tq - 1);
+        dma4(mask_addr + k * 256, a.mask_bits + ((int64_t)b * a.Tq + r) * a.W + n % a.W);
+      }
+      if (a.S > 0 && wave == C::kWaves - 1)
+        dma4((uint32_t)(uintptr_t)(lds_char*)(char*)sp_lds, a.sp_bits + (int64_t)b * a.W + min(lane, a.W - 1));
     }
-    if (a.S > 0 && wave == C::kWaves - 1)
-      dma4((uint32_t)(uintptr_t)(lds_char*)(char*)sp_lds, a.sp_bits + (int64_t)b * a.W + min(lane, a.W - 1));
   }
 
   // The first steps' tiles follow; their HBM latency overlaps the setup's.
@@ -255,6 +287,54 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   }
   const int lx16 = ((lane ^ 16) << 2), lx32 = ((lane ^ 32) << 2);   // byte lane addresses for permutes
 
+  // ---- the block mask from the parent array (only the last split has block
+  // tiles), while the queries and first tiles are in flight.  Row r sees block
+  // key c iff r < n_q and c is r or an ancestor of r along parent links that
+  // point strictly upwards (the first link that does not ends the chain).
+  // Pointer jumping: after round k, msk[r] holds the first 2^k rows of r's
+  // chain and anc[r] the row 2^k links up (-1 past the end), so ceil(log2 Tq)
+  // rounds cover any chain, and the rounds stop as soon as no row has a link
+  // left (ceil(log2 depth) for a tree of that depth).  One buffer: each round
+  // reads, then writes.
+  if (tree && last) {
+    wait_lgkm0();
+    block_barrier();   // initial rows and links stored by every wave
+    constexpr int IPT = SPEC_MAX_TQ * ((SPEC_MAX_TQ + 31) / 32) / C::kThreads;   // items per thread at most
+    for (int k = 0; (1 << k) < a.Tq; ++k) {
+      uint32_t nv[IPT];
+      int na = -1;
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const int i = tid + j * C::kThreads;
+        if (i < a.Tq * a.W) {
+          const int r = i / a.W, w = i % a.W;
+          const int pr = anc_l[r];
+          nv[j] = msk_l[i] | (pr >= 0 ? msk_l[pr * a.W + w] : 0u);
+        }
+      }
+      if (tid < a.Tq) {
+        const int pr = anc_l[tid];
+        na = pr >= 0 ? anc_l[pr] : -1;
+      }
+      wait_lgkm0();
+      block_barrier();
+#pragma unroll
+      for (int j = 0; j < IPT; ++j) {
+        const int i = tid + j * C::kThreads;
+        if (i < a.Tq * a.W) msk_l[i] = nv[j];
+      }
+      if (tid < a.Tq) anc_l[tid] = na;
+      // the barrier (with its fences) that ends the round also tells whether any link is left
+      if (!__syncthreads_or(na >= 0)) break;
+    }
+    for (int i = tid; i < C::ROWS * a.W; i += C::kThreads) {
+      const int rl = i / a.W, w = i % a.W;
+      const int r = min((row0 + rl) / a.G, a.Tq - 1);
+      mask_lds[i] = msk_l[r * a.W + w];
+    }
+    // published by the barrier below (after this wave's stores have completed)
+  }
+
   // The wave's setup loads have landed once no more than its tile loads are in
   // flight (K loaders issued P/2 steps of them, V loaders P/2 - 1: their first
   // step has no tile); after the barrier every wave's have.
@@ -264,6 +344,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     wait_vmcnt<(C::P / 2 - 1) * C::LPS>();
   else
     wait_vmcnt<(C::P / 2) * C::LPS>();
+  wait_lgkm0();   // this wave's LDS stores (the parents and flags) are done before the barrier
   block_barrier();
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -276,7 +357,10 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       qf[nb][dc] = as_bf16x8(v);
     }
     const int r = row_r[nb];
-    row_sp[nb] = row_ok[nb] && a.S > 0 && ((sp_lds[min(r, a.Tq - 1) >> 5] >> (r & 31)) & 1u);
+    if (tree)
+      row_sp[nb] = row_ok[nb] && a.S > 0 && spf_l[min(r, a.Tq - 1)] != 0;   // stored before the barrier above
+    else
+      row_sp[nb] = row_ok[nb] && a.S > 0 && ((sp_lds[min(r, a.Tq - 1) >> 5] >> (r & 31)) & 1u);
   }
   // the staged queries are overwritten by step P/2's V loads, issued only after
   // a barrier that every wave reaches after this
@@ -677,6 +761,8 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       xm[((wq * NB + nb) * 64 + lane) * 2 + 0] = mrun[nb];
       xm[((wq * NB + nb) * 64 + lane) * 2 + 1] = lrun[nb];
     }
+    // the barrier below does not wait for memory operations: publish the stores
+    wait_lgkm0();
   }
   block_barrier();
   if (grp == 1) return;
@@ -733,19 +819,19 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
   const int64_t nwg = (int64_t)a.n_split * a.row_chunks * a.B * a.Hkv;
   const dim3 grid((unsigned)nwg);
   const dim3 block(512);
-  auto go = [&](auto vt) {
+  auto go = [&](auto vt) -> hipError_t {
     constexpr bool VT = decltype(vt)::value;
+    // 128-row workgroups run at D = 128 only (the plan gives D = 64 64-row workgroups)
     if (a.rows_per_wg == 128) {
-      if (a.D == 128) hipLaunchKernelGGL((k_attn_mfma<128, 2, VT>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((k_attn_mfma<64, 2, VT>), grid, block, 0, st, a);
+      if (a.D != 128) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_attn_mfma<128, 2, VT>), grid, block, 0, st, a);
     } else {
       if (a.D == 128) hipLaunchKernelGGL((k_attn_mfma<128, 1, VT>), grid, block, 0, st, a);
       else hipLaunchKernelGGL((k_attn_mfma<64, 1, VT>), grid, block, 0, st, a);
     }
+    return hipGetLastError();
   };
-  if (a.v_tiled) go(std::true_type{});
-  else go(std::false_type{});
-  return hipGetLastError();
+  return a.v_tiled ? go(std::true_type{}) : go(std::false_type{});
 }
 
 }  // namespace sv

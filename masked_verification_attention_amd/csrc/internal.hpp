@@ -38,6 +38,11 @@ struct AttnArgs {
   int row_chunks;                   // MFMA path: row chunks per (request, kv-head)
   int rows_per_wg;                  // MFMA path: 64 or 128 rows per workgroup
   int v_tiled;                      // V cache in SPEC_V_TILE32 layout (MFMA path only)
+  // mask_from_parent: the block mask is built inside the kernel from attn_parent
+  // and sp_flag (spec_verify_attn_tree) instead of read from mask_bits / sp_bits
+  int mask_from_parent;
+  const int32_t* attn_parent;       // [B][Tq]
+  const uint8_t* sp_flag;           // [B][Tq] or NULL
 };
 
 enum AttnPath { PATH_VALU = 0, PATH_MFMA = 1 };

@@ -54,7 +54,8 @@ class VerifyStep:
 
     def __init__(self, cfg: VerifyConfig, x: Dict[str, np.ndarray], device="cuda", kv_splits: int = 0,
                  scale: float = 0.0, max_depth: Optional[int] = None, layout: str = "blhd",
-                 accept: str = "greedy", threshold: float = 1e-3, draft_prob=None, uniform=None):
+                 accept: str = "greedy", threshold: float = 1e-3, draft_prob=None, uniform=None,
+                 fused_mask: Optional[bool] = None):
         """``layout`` of the K/V cache in HBM: "blhd" = [B, lmax, Hkv, D] (token-major, the
         generator's order), "bhld" = [B, Hkv, lmax, D] (head-major), or "bhld_vt" = K head-major
         and V in transposed 32-key tiles [B, Hkv, lmax/32, D, 32] (SPEC_V_TILE32; lmax is
@@ -63,7 +64,9 @@ class VerifyStep:
         returns the cache in the generator's order and capacity either way.  ``accept`` selects the acceptance rule
         of ``run()``: "greedy" (hard matching), "threshold" (target probability above
         ``threshold``) or "soft" (soft matching with the given ``draft_prob`` and
-        ``uniform`` arrays [B, T])."""
+        ``uniform`` arrays [B, T]).  ``fused_mask``: ``run()`` builds the block mask inside the
+        attention launch (spec_verify_attn_tree) instead of with spec_build_mask first; by
+        default wherever that entry point applies (bf16 inputs, parent-array masks)."""
         self.cfg = cfg
         self.device = torch.device(device)
         dt = cfg.dtype
@@ -115,6 +118,10 @@ class VerifyStep:
         # the verification rows
         self.msa = cfg.structure == "msa_tree"
         self.tree_parent = to_device(x["tree_parent"], "i32", dev) if self.msa else None
+        can_fuse = not self.msa and cfg.dtype == "bf16"
+        if fused_mask and not can_fuse:
+            raise ValueError("the fused mask build needs bf16 inputs and a parent-array mask")
+        self.fused_mask = can_fuse if fused_mask is None else bool(fused_mask)
 
         i32 = dict(dtype=torch.int32, device=dev)
         self.mask_bits = torch.zeros(self.B, self.Tq, self.W, **i32)
@@ -186,6 +193,14 @@ class VerifyStep:
                             self.out if out is None else out, self.lse if lse == "self" else lse,
                             self.workspace, self.ws_bytes, stream)
 
+    def attention_tree(self, stream=None, out=None, lse="self"):
+        """Mask build and attention in one launch (spec_verify_attn_tree); mask_bits and
+        sp_bits are neither read nor written."""
+        bd.spec_verify_attn_tree(self.desc, self.q, self.k_cache, self.v_cache, self.cache_len, self.k_blk,
+                                 self.v_blk, self.k_soft, self.v_soft, self.attn_parent, self.sp_flag, self.n_q,
+                                 self.out if out is None else out, self.lse if lse == "self" else lse,
+                                 self.workspace, self.ws_bytes, stream)
+
     def argmax_accept(self, stream=None):
         if self.msa:
             bd.spec_argmax_accept_rows(self.logits, DTYPE_CODE[self.cfg.logits_dtype], self.B, self.T, self.V,
@@ -240,8 +255,11 @@ class VerifyStep:
     def run(self, stream=None):
         """One pass of the whole hot path (the cache length is not advanced in place);
         multi-stream workloads also draft the next tree in the same pass."""
-        self.build_mask(stream)
-        self.attention(stream)
+        if self.fused_mask:
+            self.attention_tree(stream)
+        else:
+            self.build_mask(stream)
+            self.attention(stream)
         self.tail(stream)
 
     def prepare(self, stream=None):
@@ -249,15 +267,21 @@ class VerifyStep:
         zero-argument callables (mask, attention, tail) on ``stream``."""
         P = bd.Prepared
         dt = DTYPE_CODE[self.cfg.logits_dtype]
-        if self.msa:
-            mask = [P("spec_build_msa_mask", self.tree_parent, self.n_nodes, self.B, self.tree_parent.shape[1],
-                      self.cfg.gamma, self.Tq, self.mask_bits, self.sp_bits, self.n_q, stream=stream)]
+        if self.fused_mask:
+            mask = []
+            attn = [P("spec_verify_attn_tree", self.desc, self.q, self.k_cache, self.v_cache, self.cache_len,
+                      self.k_blk, self.v_blk, self.k_soft, self.v_soft, self.attn_parent, self.sp_flag, self.n_q,
+                      self.out, self.lse, self.workspace, int(self.ws_bytes), stream=stream)]
         else:
-            mask = [P("spec_build_mask", self.attn_parent, self.sp_flag, self.n_q, self.B, self.Tq, self.mask_bits,
-                      self.sp_bits, stream=stream)]
-        attn = [P("spec_verify_attn", self.desc, self.q, self.k_cache, self.v_cache, self.cache_len, self.k_blk,
-                  self.v_blk, self.k_soft, self.v_soft, self.mask_bits, self.sp_bits, self.n_q, self.out, self.lse,
-                  self.workspace, int(self.ws_bytes), stream=stream)]
+            if self.msa:
+                mask = [P("spec_build_msa_mask", self.tree_parent, self.n_nodes, self.B, self.tree_parent.shape[1],
+                          self.cfg.gamma, self.Tq, self.mask_bits, self.sp_bits, self.n_q, stream=stream)]
+            else:
+                mask = [P("spec_build_mask", self.attn_parent, self.sp_flag, self.n_q, self.B, self.Tq,
+                          self.mask_bits, self.sp_bits, stream=stream)]
+            attn = [P("spec_verify_attn", self.desc, self.q, self.k_cache, self.v_cache, self.cache_len, self.k_blk,
+                      self.v_blk, self.k_soft, self.v_soft, self.mask_bits, self.sp_bits, self.n_q, self.out,
+                      self.lse, self.workspace, int(self.ws_bytes), stream=stream)]
         vrow = self.acc_parent if self.msa else None
         if self.accept == "greedy":
             tail = [P("spec_argmax_accept_commit", self.logits, dt, self.T, self.V, self.n_nodes, self.draft_tok,

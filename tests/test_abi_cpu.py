@@ -272,3 +272,45 @@ def test_v_layout_validation():
         with pytest.raises(bd.SpecError) as e:
             bd.spec_commit_kv(desc, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, stream=0)
         assert e.value.status == status
+
+
+def test_attn_tree_validation_before_any_hip_call():
+    F = FAKE
+
+    def tree(desc, parent=F, flags=F, q=F, out=F, ws=None, ws_bytes=0, soft=True):
+        ks = F if (desc.S and soft) else None
+        bd.spec_verify_attn_tree(desc, q, F, F, F, F, F, ks, ks, parent, flags, F, out, None, ws, ws_bytes,
+                                 stream=0)
+
+    # fp32 inputs take the two-call path
+    with pytest.raises(bd.SpecError) as e:
+        tree(good_desc(dtype=bd.SPEC_F32))
+    assert e.value.status == bd.SPEC_EUNSUPPORTED and "bf16" in str(e.value)
+    # the parent array is required and word-aligned; the byte flags need no alignment
+    with pytest.raises(bd.SpecError) as e:
+        tree(good_desc(), parent=None)
+    assert e.value.status == bd.SPEC_EINVAL and "attn_parent" in str(e.value)
+    with pytest.raises(bd.SpecError) as e:
+        tree(good_desc(), parent=F + 2)
+    assert e.value.status == bd.SPEC_EINVAL and "4-byte aligned" in str(e.value)
+    # spec_verify_attn's other checks apply
+    with pytest.raises(bd.SpecError) as e:
+        tree(good_desc(), q=F + 4)
+    assert e.value.status == bd.SPEC_EINVAL and "16-byte aligned" in str(e.value)
+    with pytest.raises(bd.SpecError) as e:
+        tree(good_desc(), out=None)
+    assert e.value.status == bd.SPEC_EINVAL
+    # soft prompt rows: k_soft / v_soft are needed, sp_flag is not
+    with pytest.raises(bd.SpecError) as e:
+        tree(good_desc(S=16), soft=False)
+    assert e.value.status == bd.SPEC_EINVAL and "k_soft" in str(e.value)
+    # a split plan needs its workspace, as spec_verify_attn
+    desc = good_desc(kv_splits=4)
+    need = bd.spec_verify_attn_workspace(desc)
+    assert need > 0
+    with pytest.raises(bd.SpecError) as e:
+        tree(desc, ws=F, ws_bytes=need - 1)
+    assert e.value.status == bd.SPEC_EWORKSPACE
+    # B == 0 is a no-op that touches no device
+    bd.spec_verify_attn_tree(good_desc(B=0), None, None, None, None, None, None, None, None, None, None, None,
+                             None, None, None, 0, stream=0)

@@ -417,6 +417,8 @@ def test_full_size_sampled(name, layout):
     st = VerifyStep(cfg, x, layout=layout)
     say(f"[gpu] full-size {name}: run step (ws {st.ws_bytes} B)")
     st.run()
+    if st.fused_mask:   # run() built the mask inside the attention launch; check the mask kernel too
+        st.build_mask()
     torch.cuda.synchronize()
     bits, sp = oracle.build_mask(x["attn_parent"], x["sp_flag"], x["n_q"])
     np.testing.assert_array_equal(st.mask_bits.cpu().numpy().view(np.uint32), bits)

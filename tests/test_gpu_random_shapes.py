@@ -63,19 +63,22 @@ def draw_case(i):
     splits = int(rng.choice([0, 0, 2, 5]))
     V = int(rng.choice([1003, 4096, 32000]))
     cfg = cfg.with_(V=V)
-    return cfg, B, layout, splits
+    fused = bool(rng.integers(0, 2)) and cfg.dtype == "bf16" and cfg.structure != "msa_tree"
+    return cfg, B, layout, splits, fused
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape_step(i):
-    cfg, B, layout, splits = draw_case(i)
+    cfg, B, layout, splits, fused = draw_case(i)
     if cfg.structure == "msa_tree" and cfg.Tq > 256:
         pytest.skip("block over 256 rows")
     say(f"[gpu] {cfg.name}: B={B} Hq/Hkv={cfg.Hq}/{cfg.Hkv} D={cfg.D} Tq={cfg.Tq} S={cfg.S} L={cfg.L} "
-        f"{cfg.dtype} {layout} splits={splits} V={cfg.V}")
+        f"{cfg.dtype} {layout} splits={splits} V={cfg.V} fused mask={fused}")
     x = wl.generate(cfg, B=B)
-    st = VerifyStep(cfg, x, layout=layout, kv_splits=splits)
+    st = VerifyStep(cfg, x, layout=layout, kv_splits=splits, fused_mask=fused)
     st.run()
+    if fused:
+        st.build_mask()   # the mask kernel is checked as well
     torch.cuda.synchronize()
     if cfg.structure == "msa_tree":
         bits, _, nq = oracle.build_msa_mask(x["tree_parent"], x["n_nodes"], cfg.gamma, cfg.Tq)
