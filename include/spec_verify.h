@@ -16,6 +16,7 @@
  *   spec_verify_attn_noalloc  the same without a workspace argument (for
  *                       callers that cannot allocate)
  *   spec_verify_attn_tree  mask build and attention in one launch
+ *   spec_verify_attn_msa   multi-stream mask build and attention in one launch
  *   spec_argmax_accept  per-node greedy token, longest accepted path
  *   spec_argmax_accept_rows  the same with explicit verification rows, an
  *                       explicit root and the correction token
@@ -359,6 +360,38 @@ int spec_verify_attn_tree(const spec_attn_desc* d, const void* q,
                           const int32_t* attn_parent, const uint8_t* sp_flag, const int32_t* n_q,
                           float* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * spec_verify_attn_msa -- spec_build_msa_mask and spec_verify_attn in one
+ * launch: the attention builds the multi-stream rows' masks itself from the
+ * node tree ([SS] Multi-Stream Attention, Equations 1 and 2 over the tree
+ * draft of Equation 4, and the batching paragraph: (1 + gamma) rows per node),
+ * with the rule and row layout of spec_build_msa_mask: rows 0..n-1 are the
+ * main streams of nodes 0..n-1, row n + v*gamma + (j-1) is stream j of node v;
+ * a main row sees the main rows of its node's root path (tree-parent links
+ * that point strictly upwards), stream j of v sees those and streams 1..j of
+ * v; n = clamp(n_nodes[b], 0, N), and rows from n * (1 + gamma) on are padding.
+ * No row sees the soft prompt.
+ *
+ *   tree_parent [B, N] int32   node parents, -1 = the root's parent (4-byte aligned)
+ *   n_nodes     [B] int32      nodes per request (takes the place of n_q)
+ *   N, gamma                   as spec_build_msa_mask: 1 <= N, 0 <= gamma,
+ *                              N * (1 + gamma) <= Tq
+ * Every other argument, the workspace (spec_verify_attn_workspace) and the
+ * results are those of spec_verify_attn; out and lse are bitwise equal to
+ * spec_build_msa_mask followed by spec_verify_attn on the same inputs.  The
+ * row counts n_q are not written (spec_build_msa_mask writes them).
+ *
+ * bf16 inputs only; fp32 inputs return SPEC_EUNSUPPORTED.  Errors otherwise
+ * as spec_verify_attn and spec_build_msa_mask.
+ */
+int spec_verify_attn_msa(const spec_attn_desc* d, const void* q,
+                         const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                         const void* k_blk, const void* v_blk,
+                         const void* k_soft, const void* v_soft,
+                         const int32_t* tree_parent, const int32_t* n_nodes, int32_t N, int32_t gamma,
+                         float* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * spec_verify_attn_noalloc -- spec_verify_attn without a workspace argument,

@@ -38,7 +38,7 @@ SPEC_ACCEPT_SOFT = 2
 
 # every symbol the header declares
 EXPORTS = ("spec_build_mask", "spec_build_msa_mask", "spec_verify_attn_workspace", "spec_verify_attn",
-           "spec_verify_attn_noalloc", "spec_verify_attn_tree",
+           "spec_verify_attn_noalloc", "spec_verify_attn_tree", "spec_verify_attn_msa",
            "spec_argmax_accept", "spec_argmax_accept_rows", "spec_prob_accept", "spec_commit_kv",
            "spec_argmax_accept_commit", "spec_draft_tree",
            "spec_strerror", "spec_last_error", "spec_version")
@@ -97,6 +97,9 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_attn_noalloc.restype = ctypes.c_int
     lib.spec_verify_attn_tree.argtypes = [ctypes.POINTER(AttnDesc)] + [_P] * 14 + [ctypes.c_size_t, _P]
     lib.spec_verify_attn_tree.restype = ctypes.c_int
+    lib.spec_verify_attn_msa.argtypes = [ctypes.POINTER(AttnDesc)] + [_P] * 10 + [_I, _I] + [_P] * 3 + \
+        [ctypes.c_size_t, _P]
+    lib.spec_verify_attn_msa.restype = ctypes.c_int
     lib.spec_argmax_accept.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P]
     lib.spec_argmax_accept.restype = ctypes.c_int
     lib.spec_argmax_accept_rows.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P]
@@ -223,6 +226,17 @@ def spec_verify_attn_tree(desc: AttnDesc, q, k_cache, v_cache, cache_len, k_blk,
                                      _ptr(sp_flag), _ptr(n_q), _ptr(out), _ptr(lse), _ptr(workspace),
                                      int(workspace_bytes), _stream(stream) if desc.B else None),
            "spec_verify_attn_tree")
+
+
+def spec_verify_attn_msa(desc: AttnDesc, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft,
+                         tree_parent, n_nodes, N, gamma, out, lse=None, workspace=None, workspace_bytes=0,
+                         stream=None):
+    lib = load()
+    _check(lib.spec_verify_attn_msa(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len),
+                                    _ptr(k_blk), _ptr(v_blk), _ptr(k_soft), _ptr(v_soft), _ptr(tree_parent),
+                                    _ptr(n_nodes), int(N), int(gamma), _ptr(out), _ptr(lse), _ptr(workspace),
+                                    int(workspace_bytes), _stream(stream) if desc.B else None),
+           "spec_verify_attn_msa")
 
 
 def spec_argmax_accept(logits, logits_dtype, B, T, V, n_nodes, draft_tok, acc_parent, max_depth,

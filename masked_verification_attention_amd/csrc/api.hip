@@ -350,13 +350,21 @@ int check_attn_args(const char* fn, const spec_attn_desc* d, const void* q, cons
 }
 
 // Enqueue a validated call; `workspace` holds at least plan.ws_bytes bytes.
-// attn_parent != NULL: the kernel builds the block mask from attn_parent /
-// sp_flag (spec_verify_attn_tree) and mask_bits / sp_bits are not read.
+// Where the kernel's block mask comes from (mask_bits / sp_bits / n_q, or built
+// in the kernel: see sv::MaskMode); only the pointers of that source are read.
+struct MaskSource {
+  sv::MaskMode mode = sv::MASK_WORDS;
+  const int32_t* parent = nullptr;   // attn_parent (MASK_PARENT) or tree_parent (MASK_MSA)
+  const uint8_t* sp_flag = nullptr;
+  const int32_t* n_nodes = nullptr;
+  int N = 0, gamma = 0;
+};
+
 int launch_verify_attn(const spec_attn_desc* d, const sv::AttnPlan& plan, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* cache_len, const void* k_blk, const void* v_blk,
                        const void* k_soft, const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
                        const int32_t* n_q, float* out, float* lse, void* workspace, void* stream,
-                       const int32_t* attn_parent = nullptr, const uint8_t* sp_flag = nullptr) {
+                       const MaskSource& ms = MaskSource()) {
   sv::AttnArgs a{};
   a.B = d->B;
   a.Tq = d->Tq;
@@ -390,9 +398,12 @@ int launch_verify_attn(const spec_attn_desc* d, const sv::AttnPlan& plan, const 
   a.row_chunks = plan.row_chunks;
   a.rows_per_wg = plan.rows_per_wg;
   a.v_tiled = d->v_layout == SPEC_V_TILE32;
-  a.mask_from_parent = attn_parent != nullptr;
-  a.attn_parent = attn_parent;
-  a.sp_flag = sp_flag;
+  a.mask_mode = ms.mode;
+  a.attn_parent = ms.parent;
+  a.sp_flag = ms.sp_flag;
+  a.n_nodes = ms.n_nodes;
+  a.msa_N = ms.N;
+  a.msa_gamma = ms.gamma;
   if (plan.n_split > 1) {
     const size_t rows = (size_t)plan.n_split * d->B * d->Hkv * a.R;
     char* ws = static_cast<char*>(workspace);
@@ -477,8 +488,49 @@ int spec_verify_attn_tree(const spec_attn_desc* d, const void* q, const void* k_
             "workspace of %zu bytes needed, %zu given", plan.ws_bytes, workspace ? workspace_bytes : 0);
     REQUIRE(aligned(workspace, 16), SPEC_EINVAL, "workspace must be 16-byte aligned");
   }
+  MaskSource ms;
+  ms.mode = sv::MASK_PARENT;
+  ms.parent = attn_parent;
+  ms.sp_flag = sp_flag;
   return launch_verify_attn(d, plan, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft, nullptr,
-                            nullptr, n_q, out, lse, workspace, stream, attn_parent, sp_flag);
+                            nullptr, n_q, out, lse, workspace, stream, ms);
+}
+
+int spec_verify_attn_msa(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
+                         const void* v_soft, const int32_t* tree_parent, const int32_t* n_nodes, int32_t N,
+                         int32_t gamma, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  static const char* fn = "spec_verify_attn_msa";
+  const int st0 = check_desc(d);
+  if (st0 != SPEC_OK) return st0;
+  REQUIRE(gamma >= 0 && gamma < SPEC_MAX_TQ, SPEC_EINVAL, "%s: gamma = %d outside [0, %d)", fn, gamma, SPEC_MAX_TQ);
+  REQUIRE(N >= 1 && N <= SPEC_MAX_TQ, SPEC_EINVAL, "%s: N = %d outside [1, %d]", fn, N, SPEC_MAX_TQ);
+  REQUIRE((int64_t)N * (1 + gamma) <= d->Tq, SPEC_EINVAL, "%s: N * (1 + gamma) = %lld rows exceed Tq = %d", fn,
+          (long long)N * (1 + gamma), d->Tq);
+  if (d->B == 0) return ok();
+  REQUIRE(d->dtype == SPEC_BF16, SPEC_EUNSUPPORTED,
+          "%s: bf16 inputs only (fp32 inputs: spec_build_msa_mask, then spec_verify_attn)", fn);
+  // spec_verify_attn's checks, the node tree in place of the mask and n_nodes in place of n_q
+  REQUIRE(tree_parent != nullptr, SPEC_EINVAL, "%s: tree_parent must be non-NULL", fn);
+  REQUIRE(n_nodes != nullptr, SPEC_EINVAL, "%s: n_nodes must be non-NULL", fn);
+  const int st = check_attn_args(fn, d, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft, tree_parent,
+                                 nullptr, n_nodes, out, lse, /*tree=*/true);
+  if (st != SPEC_OK) return st;
+  const sv::AttnPlan plan = sv::plan_attn(*d);
+  if (plan.ws_bytes > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= plan.ws_bytes, SPEC_EWORKSPACE,
+            "workspace of %zu bytes needed, %zu given", plan.ws_bytes, workspace ? workspace_bytes : 0);
+    REQUIRE(aligned(workspace, 16), SPEC_EINVAL, "workspace must be 16-byte aligned");
+  }
+  MaskSource ms;
+  ms.mode = sv::MASK_MSA;
+  ms.parent = tree_parent;
+  ms.n_nodes = n_nodes;
+  ms.N = N;
+  ms.gamma = gamma;
+  return launch_verify_attn(d, plan, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft, v_soft, nullptr,
+                            nullptr, nullptr, out, lse, workspace, stream, ms);
 }
 
 int spec_verify_attn_noalloc(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,

@@ -94,7 +94,9 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   const int q4 = lane >> 4;
 
   const int L = (int)min<int64_t>(max(a.cache_len[b], 0), a.lmax);
-  const int nq = clampi(a.n_q[b], 0, a.Tq);
+  // multi-stream rows: n nodes, each with its main row and gamma stream rows
+  const int msa_n = a.mask_mode == MASK_MSA ? clampi(a.n_nodes[b], 0, a.msa_N) : 0;
+  const int nq = a.mask_mode == MASK_MSA ? min(msa_n * (1 + a.msa_gamma), a.Tq) : clampi(a.n_q[b], 0, a.Tq);
   // split boundaries on 32-key multiples, so a split's prefix tiles are the cache's tiles
   const int keys_per_split = (((L + a.n_split - 1) / a.n_split) + C::TK - 1) / C::TK * C::TK;
   const int ks = min(L, split * keys_per_split);
@@ -196,14 +198,19 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   // in V slots 4..7, which the tile stream first writes at step P/2), the mask
   // words of its rows and the request's soft-prompt words.  Rows past the end
   // or past the request's queries read an in-range row; the values are not used.
-  // When the mask is built here from the parent array (mask_from_parent), the
-  // parents and soft-prompt flags come first instead, with plain loads (one per
-  // thread) consumed before any direct-to-LDS load is issued, so their waits
-  // cover nothing else; their latency overlaps that of the cache length.  The
-  // mask is then built in LDS while the queries and first tiles are in flight,
-  // in slots that the tile stream first writes at step P/2: the mask rows in
-  // K slots 6.. (8 KB), the ancestor links and flags after them.
-  const bool tree = a.mask_from_parent != 0;
+  // When the mask is built here (from the parent array, or from the node tree
+  // of multi-stream rows), the parents and soft-prompt flags come first
+  // instead, with plain loads (one per thread) consumed before any
+  // direct-to-LDS load is issued, so their waits cover nothing else; their
+  // latency overlaps that of the cache length.  The mask is then built in LDS
+  // while the queries and first tiles are in flight, in slots that the tile
+  // stream first writes at step P/2: the chain masks in K slots 6.. (8 KB), the
+  // links and flags after them.  The chains run over block rows (parent
+  // array) or over tree nodes (multi-stream rows).
+  const bool tree = a.mask_mode != MASK_WORDS;
+  const bool msa = a.mask_mode == MASK_MSA;
+  const int nchain = msa ? a.msa_N : a.Tq;    // entries of the pointer jumping
+  const int nvalid = msa ? msa_n : nq;        // entries that start a chain
   static_assert(C::ROWS * D * 2 <= 2 * C::TILEB || D == 128, "at D = 64 the query stage leaves V slots 6, 7");
   uint32_t* const msk_l = reinterpret_cast<uint32_t*>(ring + 6 * C::TILEB);              // [Tq][W]
   char* const aux_l = D == 128 ? ring + 7 * C::TILEB : ring + (C::NSK + 6) * C::TILEB;
@@ -216,14 +223,14 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   if (tree) {
     int32_t pr = -1;
     uint8_t f = 0;
-    if (tid < a.Tq) {
-      pr = a.attn_parent[(int64_t)b * a.Tq + tid];
-      if (a.sp_flag != nullptr) f = a.sp_flag[(int64_t)b * a.Tq + tid];
-      // row r < n_q starts as itself, linked to its parent while the link points up
+    if (tid < nchain) {
+      pr = a.attn_parent[(int64_t)b * nchain + tid];
+      if (!msa && a.sp_flag != nullptr) f = a.sp_flag[(int64_t)b * a.Tq + tid];
+      // entry r < nvalid starts as itself, linked to its parent while the link points up
       const int r = tid;
-      anc_l[r] = (r < nq && pr >= 0 && pr < r) ? pr : -1;
+      anc_l[r] = (r < nvalid && pr >= 0 && pr < r) ? pr : -1;
       spf_l[r] = f;
-      for (int w = 0; w < a.W; ++w) msk_l[r * a.W + w] = (r < nq && (r >> 5) == w) ? 1u << (r & 31) : 0u;
+      for (int w = 0; w < a.W; ++w) msk_l[r * a.W + w] = (r < nvalid && (r >> 5) == w) ? 1u << (r & 31) : 0u;
     }
   }
   const int row0 = chunk_id * C::ROWS;
@@ -300,19 +307,19 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     wait_lgkm0();
     block_barrier();   // initial rows and links stored by every wave
     constexpr int IPT = SPEC_MAX_TQ * ((SPEC_MAX_TQ + 31) / 32) / C::kThreads;   // items per thread at most
-    for (int k = 0; (1 << k) < a.Tq; ++k) {
+    for (int k = 0; (1 << k) < nchain; ++k) {
       uint32_t nv[IPT];
       int na = -1;
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
         const int i = tid + j * C::kThreads;
-        if (i < a.Tq * a.W) {
+        if (i < nchain * a.W) {
           const int r = i / a.W, w = i % a.W;
           const int pr = anc_l[r];
           nv[j] = msk_l[i] | (pr >= 0 ? msk_l[pr * a.W + w] : 0u);
         }
       }
-      if (tid < a.Tq) {
+      if (tid < nchain) {
         const int pr = anc_l[tid];
         na = pr >= 0 ? anc_l[pr] : -1;
       }
@@ -321,16 +328,30 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < IPT; ++j) {
         const int i = tid + j * C::kThreads;
-        if (i < a.Tq * a.W) msk_l[i] = nv[j];
+        if (i < nchain * a.W) msk_l[i] = nv[j];
       }
-      if (tid < a.Tq) anc_l[tid] = na;
+      if (tid < nchain) anc_l[tid] = na;
       // the barrier (with its fences) that ends the round also tells whether any link is left
       if (!__syncthreads_or(na >= 0)) break;
     }
     for (int i = tid; i < C::ROWS * a.W; i += C::kThreads) {
       const int rl = i / a.W, w = i % a.W;
       const int r = min((row0 + rl) / a.G, a.Tq - 1);
-      mask_lds[i] = msk_l[r * a.W + w];
+      uint32_t word;
+      if (!msa) {
+        word = msk_l[r * a.W + w];
+      } else if (r >= nq) {
+        word = 0u;
+      } else {
+        // row r: main row of node v (j = 0) or its stream j; it sees the main rows
+        // of v's root path and streams 1..j of v (rows n + v gamma + 0 .. j - 1)
+        const int v = r < msa_n ? r : (r - msa_n) / a.msa_gamma;
+        const int j = r < msa_n ? 0 : (r - msa_n) % a.msa_gamma + 1;
+        word = msk_l[v * a.W + w];
+        const int lo = max(msa_n + v * a.msa_gamma, 32 * w), hi = min(msa_n + v * a.msa_gamma + j, 32 * w + 32);
+        if (lo < hi) word |= (hi - lo == 32 ? ~0u : ((1u << (hi - lo)) - 1u)) << (lo - 32 * w);
+      }
+      mask_lds[i] = word;
     }
     // published by the barrier below (after this wave's stores have completed)
   }

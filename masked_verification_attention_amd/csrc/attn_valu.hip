@@ -288,7 +288,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   const int b = (int)(row / ((int64_t)a.R * a.Hkv));
   const int r = m / a.G, g = m % a.G;
   if (r >= a.Tq) return;
-  const int nq = clampi(a.n_q[b], 0, a.Tq);
+  // rows of the request (multi-stream rows built in the attention: n_nodes * (1 + gamma))
+  const int nq = a.mask_mode == MASK_MSA ? min(clampi(a.n_nodes[b], 0, a.msa_N) * (1 + a.msa_gamma), a.Tq)
+                                         : clampi(a.n_q[b], 0, a.Tq);
   const int64_t orow = ((int64_t)b * a.Tq + r) * a.Hq + (int64_t)h * a.G + g;
   float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
   float lse = -INFINITY;

@@ -38,12 +38,19 @@ struct AttnArgs {
   int row_chunks;                   // MFMA path: row chunks per (request, kv-head)
   int rows_per_wg;                  // MFMA path: 64 or 128 rows per workgroup
   int v_tiled;                      // V cache in SPEC_V_TILE32 layout (MFMA path only)
-  // mask_from_parent: the block mask is built inside the kernel from attn_parent
-  // and sp_flag (spec_verify_attn_tree) instead of read from mask_bits / sp_bits
-  int mask_from_parent;
-  const int32_t* attn_parent;       // [B][Tq]
-  const uint8_t* sp_flag;           // [B][Tq] or NULL
+  // where the block mask comes from: MASK_WORDS = mask_bits / sp_bits / n_q
+  // (spec_verify_attn); MASK_PARENT = built in the kernel from attn_parent,
+  // sp_flag and n_q (spec_verify_attn_tree); MASK_MSA = built in the kernel from
+  // the node tree (attn_parent = tree_parent [B][msa_N], n_nodes, msa_gamma), the
+  // row count being n_nodes * (1 + gamma) (spec_verify_attn_msa)
+  int mask_mode;
+  const int32_t* attn_parent;
+  const uint8_t* sp_flag;           // [B][Tq] or NULL (MASK_PARENT)
+  const int32_t* n_nodes;           // [B] (MASK_MSA)
+  int msa_N, msa_gamma;
 };
+
+enum MaskMode { MASK_WORDS = 0, MASK_PARENT = 1, MASK_MSA = 2 };
 
 enum AttnPath { PATH_VALU = 0, PATH_MFMA = 1 };
 

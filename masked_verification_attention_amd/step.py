@@ -66,7 +66,8 @@ class VerifyStep:
         ``threshold``) or "soft" (soft matching with the given ``draft_prob`` and
         ``uniform`` arrays [B, T]).  ``fused_mask``: ``run()`` builds the block mask inside the
         attention launch (spec_verify_attn_tree) instead of with spec_build_mask first; by
-        default wherever that entry point applies (bf16 inputs, parent-array masks)."""
+        default wherever it applies (bf16 inputs); multi-stream workloads use
+        spec_verify_attn_msa, which does not write n_q (build_mask() does)."""
         self.cfg = cfg
         self.device = torch.device(device)
         dt = cfg.dtype
@@ -118,9 +119,9 @@ class VerifyStep:
         # the verification rows
         self.msa = cfg.structure == "msa_tree"
         self.tree_parent = to_device(x["tree_parent"], "i32", dev) if self.msa else None
-        can_fuse = not self.msa and cfg.dtype == "bf16"
+        can_fuse = cfg.dtype == "bf16"
         if fused_mask and not can_fuse:
-            raise ValueError("the fused mask build needs bf16 inputs and a parent-array mask")
+            raise ValueError("the fused mask build needs bf16 inputs")
         self.fused_mask = can_fuse if fused_mask is None else bool(fused_mask)
 
         i32 = dict(dtype=torch.int32, device=dev)
@@ -194,12 +195,18 @@ class VerifyStep:
                             self.workspace, self.ws_bytes, stream)
 
     def attention_tree(self, stream=None, out=None, lse="self"):
-        """Mask build and attention in one launch (spec_verify_attn_tree); mask_bits and
-        sp_bits are neither read nor written."""
+        """Mask build and attention in one launch (spec_verify_attn_tree, or spec_verify_attn_msa
+        for multi-stream rows); mask_bits, sp_bits and n_q are neither read nor written."""
+        o, l = self.out if out is None else out, self.lse if lse == "self" else lse
+        if self.msa:
+            bd.spec_verify_attn_msa(self.desc, self.q, self.k_cache, self.v_cache, self.cache_len, self.k_blk,
+                                    self.v_blk, self.k_soft, self.v_soft, self.tree_parent, self.n_nodes,
+                                    self.tree_parent.shape[1], self.cfg.gamma, o, l, self.workspace,
+                                    self.ws_bytes, stream)
+            return
         bd.spec_verify_attn_tree(self.desc, self.q, self.k_cache, self.v_cache, self.cache_len, self.k_blk,
                                  self.v_blk, self.k_soft, self.v_soft, self.attn_parent, self.sp_flag, self.n_q,
-                                 self.out if out is None else out, self.lse if lse == "self" else lse,
-                                 self.workspace, self.ws_bytes, stream)
+                                 o, l, self.workspace, self.ws_bytes, stream)
 
     def argmax_accept(self, stream=None):
         if self.msa:
@@ -269,9 +276,15 @@ class VerifyStep:
         dt = DTYPE_CODE[self.cfg.logits_dtype]
         if self.fused_mask:
             mask = []
-            attn = [P("spec_verify_attn_tree", self.desc, self.q, self.k_cache, self.v_cache, self.cache_len,
-                      self.k_blk, self.v_blk, self.k_soft, self.v_soft, self.attn_parent, self.sp_flag, self.n_q,
-                      self.out, self.lse, self.workspace, int(self.ws_bytes), stream=stream)]
+            if self.msa:
+                attn = [P("spec_verify_attn_msa", self.desc, self.q, self.k_cache, self.v_cache, self.cache_len,
+                          self.k_blk, self.v_blk, self.k_soft, self.v_soft, self.tree_parent, self.n_nodes,
+                          int(self.tree_parent.shape[1]), int(self.cfg.gamma), self.out, self.lse, self.workspace,
+                          int(self.ws_bytes), stream=stream)]
+            else:
+                attn = [P("spec_verify_attn_tree", self.desc, self.q, self.k_cache, self.v_cache, self.cache_len,
+                          self.k_blk, self.v_blk, self.k_soft, self.v_soft, self.attn_parent, self.sp_flag,
+                          self.n_q, self.out, self.lse, self.workspace, int(self.ws_bytes), stream=stream)]
         else:
             if self.msa:
                 mask = [P("spec_build_msa_mask", self.tree_parent, self.n_nodes, self.B, self.tree_parent.shape[1],

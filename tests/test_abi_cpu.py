@@ -314,3 +314,25 @@ def test_attn_tree_validation_before_any_hip_call():
     # B == 0 is a no-op that touches no device
     bd.spec_verify_attn_tree(good_desc(B=0), None, None, None, None, None, None, None, None, None, None, None,
                              None, None, None, 0, stream=0)
+
+
+def test_attn_msa_validation_before_any_hip_call():
+    F = FAKE
+
+    def msa(desc, tree=F, nodes=F, N=40, gamma=3, q=F):
+        ks = F if desc.S else None
+        bd.spec_verify_attn_msa(desc, q, F, F, F, F, F, ks, ks, tree, nodes, N, gamma, F, None, None, 0, stream=0)
+
+    d160 = dict(Tq=160, Hq=32, Hkv=32, D=64, S=0)
+    with pytest.raises(bd.SpecError) as e:
+        msa(good_desc(dtype=bd.SPEC_F32, **d160))
+    assert e.value.status == bd.SPEC_EUNSUPPORTED
+    for kw, word in [(dict(N=0), "N = 0"), (dict(gamma=-1), "gamma"), (dict(N=41), "exceed Tq"),
+                     (dict(tree=None), "tree_parent"), (dict(nodes=None), "n_nodes"),
+                     (dict(tree=F + 2), "4-byte aligned"), (dict(q=F + 4), "16-byte aligned")]:
+        with pytest.raises(bd.SpecError) as e:
+            msa(good_desc(**d160), **kw)
+        assert e.value.status == bd.SPEC_EINVAL and word in str(e.value), (kw, str(e.value))
+    # B == 0 is a no-op that touches no device
+    bd.spec_verify_attn_msa(good_desc(B=0, **d160), None, None, None, None, None, None, None, None, None, None,
+                            40, 3, None, None, None, 0, stream=0)

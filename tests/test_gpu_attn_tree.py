@@ -196,3 +196,81 @@ def test_tree_rejects_fp32_inputs():
     with pytest.raises(bd.SpecError) as e:
         st.attention_tree()
     assert e.value.status == bd.SPEC_EUNSUPPORTED
+
+
+# ---- multi-stream rows: spec_verify_attn_msa against spec_build_msa_mask + spec_verify_attn
+
+def msa_oracle_check(out, lse, x, cfg):
+    vis = np.stack([oracle.msa_block_visibility(x["tree_parent"][b], int(x["n_nodes"][b]), cfg.gamma, cfg.Tq)
+                    for b in range(out.shape[0])])
+    ref, ref_lse = oracle.verify_attention(x["q"], x["k_cache"], x["v_cache"], x["cache_len"], x["k_blk"],
+                                           x["v_blk"], None, None, None, None, x["n_q"], cfg.dtype, block_vis=vis)
+    num = den = worst = 0.0
+    for b in range(out.shape[0]):
+        nq = int(x["n_q"][b])
+        assert (out[b, nq:] == 0).all() and np.isneginf(lse[b, nq:]).all(), "padding rows"
+        g, e = out[b, :nq].astype(np.float64), ref[b, :nq]
+        assert np.isfinite(g).all()
+        worst = max(worst, float(np.abs(g - e).max()) if nq else 0.0)
+        num += float(((g - e) ** 2).sum())
+        den += float((e ** 2).sum())
+        np.testing.assert_allclose(lse[b, :nq], ref_lse[b, :nq], rtol=0, atol=2e-3)
+    rel = (num / den) ** 0.5 if den else 0.0
+    say(f"    vs oracle: max-abs {worst:.3e}, rel-L2 {rel:.3e}")
+    assert worst <= BF16_ATOL and rel <= BF16_REL_L2
+
+
+MSA_CASES = [
+    # (id, config overrides, generate overrides, kv_splits, layout)
+    ("c6_small", {}, {"B": 2, "L": (100, 300)}, 0, "bhld"),
+    ("c6_pruned_split2", {}, {"B": 3, "L": (64, 200), "n_nodes": np.array([40, 13, 0])}, 2, "bhld"),
+    ("c6_g4k2_vt", {"gamma": 4, "branch": 2, "T": 31}, {"B": 2, "L": (150, 260)}, 0, "bhld_vt"),
+    ("c6_d128_gqa", {"Hq": 32, "Hkv": 8, "D": 128}, {"B": 2, "L": (200, 333)}, 0, "bhld"),
+    ("c6_empty_prefix", {}, {"B": 2, "L": (0, 0)}, 0, "blhd"),
+]
+
+
+@pytest.mark.parametrize("case", MSA_CASES, ids=[c[0] for c in MSA_CASES])
+def test_msa_fused_equals_two_calls(case):
+    cid, cov, gov, splits, layout = case
+    cfg = wl.CONFIGS["c6_msa_1b"].with_(name=cid, **cov)
+    say(f"[gpu] attn_msa {cid}: {cov} {gov} splits={splits} {layout}")
+    x = wl.generate(cfg, with_logits=False, **gov)
+    st = VerifyStep(cfg, x, kv_splits=splits, layout=layout)
+    fo, fl, to, tl = fused_and_two_calls(st)
+    assert_bitwise(fo, to, "out")
+    assert_bitwise(fl, tl, "lse")
+    msa_oracle_check(fo, fl, x, cfg)
+
+
+@pytest.mark.parametrize("gamma,branch", [(1, 100), (2, 6), (3, 3), (0, 1)])
+def test_msa_fused_random_trees(gamma, branch):
+    # random trees over the generator's node count (any earlier node as parent: deep
+    # chains too) and ragged node counts
+    T = sum(branch ** g for g in range(gamma + 1))
+    cfg = wl.CONFIGS["c6_msa_1b"].with_(name=f"msa_g{gamma}_k{branch}", gamma=gamma, branch=branch, T=T)
+    rng = np.random.default_rng(500 + 7 * gamma + branch)
+    x = wl.generate(cfg, B=3, L=(30, 120), with_logits=False)
+    N = x["tree_parent"].shape[1]
+    for b in range(3):
+        par = np.full(N, -1, dtype=np.int32)
+        for v in range(1, N):
+            par[v] = int(rng.integers(max(0, v - 3), v)) if rng.random() < 0.6 else int(rng.integers(0, v))
+        x["tree_parent"][b] = par
+    x["n_nodes"] = np.array([N, int(rng.integers(1, N + 1)), int(rng.integers(0, min(N, 4) + 1))], dtype=np.int32)
+    x["n_q"] = (x["n_nodes"] * (1 + gamma)).astype(np.int32)
+    say(f"[gpu] attn_msa random trees gamma={gamma}: N={N} Tq={cfg.Tq} n_nodes={x['n_nodes'].tolist()}")
+    st = VerifyStep(cfg, x, layout="bhld")
+    fo, fl, to, tl = fused_and_two_calls(st)
+    assert_bitwise(fo, to, "out")
+    assert_bitwise(fl, tl, "lse")
+    msa_oracle_check(fo, fl, x, cfg)
+
+
+def test_msa_fused_full_size():
+    cfg = wl.CONFIGS["c6_msa_1b"]
+    x = wl.generate(cfg, with_logits=False)
+    st = VerifyStep(cfg, x, layout="bhld")
+    fo, fl, to, tl = fused_and_two_calls(st)
+    assert_bitwise(fo, to, "out")
+    assert_bitwise(fl, tl, "lse")

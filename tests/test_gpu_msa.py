@@ -149,6 +149,8 @@ def test_msa_step_small(case):
     st.n_q.fill_(-1)                                # the mask call must write the row counts
     say(f"[gpu] {cid}: step (Tq {st.Tq}, ws {st.ws_bytes} B)")
     st.run()
+    if st.fused_mask:   # the step built the masks inside the attention launch; check the mask kernel too
+        st.build_mask()
     torch.cuda.synchronize()
     ref_bits, ref_sp, ref_nq = oracle.build_msa_mask(x["tree_parent"], x["n_nodes"], cfg.gamma, cfg.Tq)
     np.testing.assert_array_equal(st.mask_bits.cpu().numpy().view(np.uint32), ref_bits)
@@ -219,6 +221,8 @@ def test_msa_full_size_sampled(layout):
     st = VerifyStep(cfg, x, layout=layout)
     say(f"[gpu] full-size c6_msa_1b: run step (ws {st.ws_bytes} B)")
     st.run()
+    if st.fused_mask:
+        st.build_mask()
     torch.cuda.synchronize()
     ref_bits, _, ref_nq = oracle.build_msa_mask(x["tree_parent"], x["n_nodes"], cfg.gamma, cfg.Tq)
     np.testing.assert_array_equal(st.mask_bits.cpu().numpy().view(np.uint32), ref_bits)

@@ -63,7 +63,7 @@ def draw_case(i):
     splits = int(rng.choice([0, 0, 2, 5]))
     V = int(rng.choice([1003, 4096, 32000]))
     cfg = cfg.with_(V=V)
-    fused = bool(rng.integers(0, 2)) and cfg.dtype == "bf16" and cfg.structure != "msa_tree"
+    fused = bool(rng.integers(0, 2)) and cfg.dtype == "bf16"
     return cfg, B, layout, splits, fused
 
 
