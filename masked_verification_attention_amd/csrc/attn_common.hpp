@@ -81,6 +81,12 @@ __device__ __forceinline__ void dma4(uint32_t lds, const void* src) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// 1-byte direct-to-LDS load: lane i's byte lands zero-extended as the 4-byte
+// word at LDS byte address lds + 4 i (checked on the device).
+__device__ __forceinline__ void dma1(uint32_t lds, const void* src) {
+  asm volatile("global_load_lds_ubyte %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
 // Wait until every LDS read (and scalar load) of this wave has returned.
 __device__ __forceinline__ void wait_lgkm0() {
   // vmcnt and expcnt at their maxima (unconstrained), lgkmcnt 0

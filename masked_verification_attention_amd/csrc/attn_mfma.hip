@@ -199,40 +199,19 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   // words of its rows and the request's soft-prompt words.  Rows past the end
   // or past the request's queries read an in-range row; the values are not used.
   // When the mask is built here (from the parent array, or from the node tree
-  // of multi-stream rows), the parents and soft-prompt flags come first
-  // instead, with plain loads (one per thread) consumed before any
-  // direct-to-LDS load is issued, so their waits cover nothing else; their
-  // latency overlaps that of the cache length.  The mask is then built in LDS
-  // while the queries and first tiles are in flight, in slots that the tile
-  // stream first writes at step P/2: the chain masks in K slots 6.. (8 KB), the
-  // links and flags after them.  The chains run over block rows (parent
-  // array) or over tree nodes (multi-stream rows).
+  // of multi-stream rows), the parents and soft-prompt flags come instead, by
+  // the same path (a flag byte lands as a zero-extended word), into a slot that
+  // the tile stream first writes at step P/2; after the setup barrier each
+  // thread walks one row's chain there (below).
   const bool tree = a.mask_mode != MASK_WORDS;
   const bool msa = a.mask_mode == MASK_MSA;
-  const int nchain = msa ? a.msa_N : a.Tq;    // entries of the pointer jumping
-  const int nvalid = msa ? msa_n : nq;        // entries that start a chain
-  static_assert(C::ROWS * D * 2 <= 2 * C::TILEB || D == 128, "at D = 64 the query stage leaves V slots 6, 7");
-  uint32_t* const msk_l = reinterpret_cast<uint32_t*>(ring + 6 * C::TILEB);              // [Tq][W]
-  char* const aux_l = D == 128 ? ring + 7 * C::TILEB : ring + (C::NSK + 6) * C::TILEB;
-  int32_t* const anc_l = reinterpret_cast<int32_t*>(aux_l);                              // [Tq]
-  uint8_t* const spf_l = reinterpret_cast<uint8_t*>(aux_l + SPEC_MAX_TQ * 4);              // [Tq]
-  static_assert(SPEC_MAX_TQ * ((SPEC_MAX_TQ + 31) / 32) * 4 <= 8192 && 8192 <= 2 * C::TILEB,
-                "mask rows fit in K slots 6..");
-  static_assert(SPEC_MAX_TQ * 5 <= C::TILEB, "links and flags fit in one slot");
-  static_assert(SPEC_MAX_TQ <= C::kThreads, "one parent per thread");
-  if (tree) {
-    int32_t pr = -1;
-    uint8_t f = 0;
-    if (tid < nchain) {
-      pr = a.attn_parent[(int64_t)b * nchain + tid];
-      if (!msa && a.sp_flag != nullptr) f = a.sp_flag[(int64_t)b * a.Tq + tid];
-      // entry r < nvalid starts as itself, linked to its parent while the link points up
-      const int r = tid;
-      anc_l[r] = (r < nvalid && pr >= 0 && pr < r) ? pr : -1;
-      spf_l[r] = f;
-      for (int w = 0; w < a.W; ++w) msk_l[r * a.W + w] = (r < nvalid && (r >> 5) == w) ? 1u << (r & 31) : 0u;
-    }
-  }
+  const int nchain = msa ? a.msa_N : a.Tq;    // parents: one per tree node or block row
+  char* const aux_l = ring + 6 * C::TILEB;                                               // K slot 6
+  int32_t* const par_l = reinterpret_cast<int32_t*>(aux_l);                              // [nchain]
+  uint32_t* const spf_l = reinterpret_cast<uint32_t*>(aux_l + SPEC_MAX_TQ * 4);            // [Tq]
+  static_assert(SPEC_MAX_TQ * 8 <= C::TILEB, "parents and flags fit in one slot");
+  static_assert(C::ROWS <= C::kThreads, "one workgroup row per thread");
+  const bool has_flags = !msa && a.sp_flag != nullptr;
   const int row0 = chunk_id * C::ROWS;
   constexpr int QOPS = C::ROWS * D * 2 / 1024 / C::kWaves;   // 1 KB query loads per wave
   static_assert(QOPS >= 1 && QOPS * 1024 * C::kWaves == C::ROWS * D * 2, "query staging split");
@@ -249,7 +228,16 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       dma16(ring_lds + (C::NSK + 4) * C::TILEB + (wave * QOPS + jq) * 1024,
             static_cast<const char*>(a.q) + ((((int64_t)b * a.Tq + r) * a.Hq + h * a.G + g) * D + 8 * c) * 2);
     }
-    if (!tree) {
+    if (tree) {
+      // entries 64 k .. 64 k + 63 by wave k (thread r's entry comes with its own wave's
+      // loads); lanes past the end repeat the last entry
+      if (wave * 64 < nchain) {
+        const int r = min(wave * 64 + lane, nchain - 1);
+        const uint32_t aux = (uint32_t)(uintptr_t)(lds_char*)aux_l;   // par_l, then spf_l
+        dma4(aux + wave * 256, a.attn_parent + (int64_t)b * nchain + r);
+        if (has_flags) dma1(aux + SPEC_MAX_TQ * 4 + wave * 256, a.sp_flag + (int64_t)b * a.Tq + r);
+      }
+    } else {
       const uint32_t mask_addr = (uint32_t)(uintptr_t)(lds_char*)(char*)mask_lds;
       const int nmw = C::ROWS * a.W / 64;   // ROWS is a multiple of 64: whole wave loads
       for (int k = wave; k < nmw; k += C::kWaves) {
@@ -267,6 +255,17 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < C::P / 2; ++u) issue_step(u);
   }
+  // The wave's setup loads have landed once no more than its tile loads are in
+  // flight (K loaders issued P/2 steps of them, V loaders P/2 - 1: their first
+  // step has no tile); after the barrier below every wave's have.
+  auto wait_setup = [&]() __attribute__((always_inline)) {
+    if (nt == 0)
+      wait_vmcnt<0>();
+    else if (load_v)
+      wait_vmcnt<(C::P / 2 - 1) * C::LPS>();
+    else
+      wait_vmcnt<(C::P / 2) * C::LPS>();
+  };
 
   // ---- this lane's rows
   int row_r[NB], row_j[NB], row_l[NB];
@@ -294,78 +293,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   }
   const int lx16 = ((lane ^ 16) << 2), lx32 = ((lane ^ 32) << 2);   // byte lane addresses for permutes
 
-  // ---- the block mask from the parent array (only the last split has block
-  // tiles), while the queries and first tiles are in flight.  Row r sees block
-  // key c iff r < n_q and c is r or an ancestor of r along parent links that
-  // point strictly upwards (the first link that does not ends the chain).
-  // Pointer jumping: after round k, msk[r] holds the first 2^k rows of r's
-  // chain and anc[r] the row 2^k links up (-1 past the end), so ceil(log2 Tq)
-  // rounds cover any chain, and the rounds stop as soon as no row has a link
-  // left (ceil(log2 depth) for a tree of that depth).  One buffer: each round
-  // reads, then writes.
-  if (tree && last) {
-    wait_lgkm0();
-    block_barrier();   // initial rows and links stored by every wave
-    constexpr int IPT = SPEC_MAX_TQ * ((SPEC_MAX_TQ + 31) / 32) / C::kThreads;   // items per thread at most
-    for (int k = 0; (1 << k) < nchain; ++k) {
-      uint32_t nv[IPT];
-      int na = -1;
-#pragma unroll
-      for (int j = 0; j < IPT; ++j) {
-        const int i = tid + j * C::kThreads;
-        if (i < nchain * a.W) {
-          const int r = i / a.W, w = i % a.W;
-          const int pr = anc_l[r];
-          nv[j] = msk_l[i] | (pr >= 0 ? msk_l[pr * a.W + w] : 0u);
-        }
-      }
-      if (tid < nchain) {
-        const int pr = anc_l[tid];
-        na = pr >= 0 ? anc_l[pr] : -1;
-      }
-      wait_lgkm0();
-      block_barrier();
-#pragma unroll
-      for (int j = 0; j < IPT; ++j) {
-        const int i = tid + j * C::kThreads;
-        if (i < nchain * a.W) msk_l[i] = nv[j];
-      }
-      if (tid < nchain) anc_l[tid] = na;
-      // the barrier (with its fences) that ends the round also tells whether any link is left
-      if (!__syncthreads_or(na >= 0)) break;
-    }
-    for (int i = tid; i < C::ROWS * a.W; i += C::kThreads) {
-      const int rl = i / a.W, w = i % a.W;
-      const int r = min((row0 + rl) / a.G, a.Tq - 1);
-      uint32_t word;
-      if (!msa) {
-        word = msk_l[r * a.W + w];
-      } else if (r >= nq) {
-        word = 0u;
-      } else {
-        // row r: main row of node v (j = 0) or its stream j; it sees the main rows
-        // of v's root path and streams 1..j of v (rows n + v gamma + 0 .. j - 1)
-        const int v = r < msa_n ? r : (r - msa_n) / a.msa_gamma;
-        const int j = r < msa_n ? 0 : (r - msa_n) % a.msa_gamma + 1;
-        word = msk_l[v * a.W + w];
-        const int lo = max(msa_n + v * a.msa_gamma, 32 * w), hi = min(msa_n + v * a.msa_gamma + j, 32 * w + 32);
-        if (lo < hi) word |= (hi - lo == 32 ? ~0u : ((1u << (hi - lo)) - 1u)) << (lo - 32 * w);
-      }
-      mask_lds[i] = word;
-    }
-    // published by the barrier below (after this wave's stores have completed)
-  }
-
-  // The wave's setup loads have landed once no more than its tile loads are in
-  // flight (K loaders issued P/2 steps of them, V loaders P/2 - 1: their first
-  // step has no tile); after the barrier every wave's have.
-  if (nt == 0)
-    wait_vmcnt<0>();
-  else if (load_v)
-    wait_vmcnt<(C::P / 2 - 1) * C::LPS>();
-  else
-    wait_vmcnt<(C::P / 2) * C::LPS>();
-  wait_lgkm0();   // this wave's LDS stores (the parents and flags) are done before the barrier
+  wait_setup();
   block_barrier();
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -379,12 +307,54 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     }
     const int r = row_r[nb];
     if (tree)
-      row_sp[nb] = row_ok[nb] && a.S > 0 && spf_l[min(r, a.Tq - 1)] != 0;   // stored before the barrier above
+      row_sp[nb] = row_ok[nb] && a.S > 0 && has_flags && spf_l[min(r, a.Tq - 1)] != 0u;
     else
       row_sp[nb] = row_ok[nb] && a.S > 0 && ((sp_lds[min(r, a.Tq - 1) >> 5] >> (r & 31)) & 1u);
   }
+  // ---- the block mask of the workgroup's rows from the parents (only the last
+  // split has block tiles), one row per thread, while the first tiles are in
+  // flight.  Row r sees block key c iff r < n_q and c is r or an ancestor of r
+  // along parent links that point strictly upwards (the first link that does
+  // not ends the chain).  Multi-stream rows: the chain runs over the tree
+  // nodes from the row's node v, and stream j of v also sees streams 1..j of
+  // v (rows n + v gamma .. + j - 1).  The walk of a chain of depth d takes d
+  // dependent LDS reads; the words stay in registers.
+  if (tree && last && tid < C::ROWS) {
+    const int rl = tid;
+    const int r = min((row0 + rl) / a.G, a.Tq - 1);
+    uint32_t wv[C::MAXW];
+#pragma unroll
+    for (int w = 0; w < C::MAXW; ++w) wv[w] = 0u;
+    auto set_bit = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < C::MAXW; ++w) wv[w] |= (c >> 5) == w ? 1u << (c & 31) : 0u;
+    };
+    if (r < nq) {
+      int cur = r, j = 0;
+      if (msa && r >= msa_n) {
+        cur = (r - msa_n) / a.msa_gamma;
+        j = (r - msa_n) % a.msa_gamma + 1;
+      }
+      const int node = cur;
+      set_bit(cur);
+      for (int pr = par_l[cur]; pr >= 0 && pr < cur; pr = par_l[pr]) {
+        set_bit(pr);
+        cur = pr;
+      }
+      if (j > 0) {
+        const int s0 = msa_n + node * a.msa_gamma;
+#pragma unroll
+        for (int w = 0; w < C::MAXW; ++w) {
+          const int lo = max(s0, 32 * w), hi = min(s0 + j, 32 * w + 32);
+          if (lo < hi) wv[w] |= (hi - lo == 32 ? ~0u : ((1u << (hi - lo)) - 1u)) << (lo - 32 * w);
+        }
+      }
+    }
+    for (int w = 0; w < a.W; ++w) mask_lds[rl * a.W + w] = wv[w];
+  }
   // the staged queries are overwritten by step P/2's V loads, issued only after
-  // a barrier that every wave reaches after this
+  // a barrier that every wave reaches after this; the mask words are read after
+  // many barriers
   wait_lgkm0();
 
   const float P_LIMIT = 256.0f;   // 2^TAU with TAU = 8: bound on any probability between rescales
