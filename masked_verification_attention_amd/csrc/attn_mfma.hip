@@ -522,33 +522,54 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     };
     // softmax of a tile that needs masking: ragged prefix tail (seg 0), soft
     // prompt (seg 1), block rows (seg 2, whose mask words the caller read: mw)
+    // A hidden key's probability is its computed value with every bit cleared
+    // (+0 whatever the slot holds, NaN included); the masked scores (-inf where
+    // hidden) are formed only when a rescale needs them.  One rescale branch
+    // for all row blocks, as in softmax_full.
     auto softmax_masked = [&](int seg, int lim, const uint32_t (&mw)[NB]) __attribute__((always_inline)) {
       // keys below lim: slots e < 4 hold keys 4 q4 + e, slots e >= 4 keys 16 + 4 q4 + e - 4
       const int nlo = clampi(lim - 4 * q4, 0, 4), nhi = clampi(lim - 16 - 4 * q4, 0, 4);
       const uint32_t in_tile = ((1u << nlo) - 1u) | (((1u << nhi) - 1u) << 4);
+      uint32_t vis[NB];
+      float p[NB][8], ps[NB];
+      bool need[NB], any_need = false;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // visibility of the lane's 8 keys (tile keys 16 kb + 4 q4 + i) for its row
-        uint32_t vis;
         if (seg == 0)
-          vis = row_ok[nb] ? 0xffu : 0u;
+          vis[nb] = row_ok[nb] ? 0xffu : 0u;
         else if (seg == 1)
-          vis = row_sp[nb] ? 0xffu : 0u;
+          vis[nb] = row_sp[nb] ? 0xffu : 0u;
         else
-          vis = ((mw[nb] >> (4 * q4)) & 0xfu) | (((mw[nb] >> (16 + 4 * q4)) & 0xfu) << 4);
-        vis &= in_tile;
-        float xs[8], p[8];
+          vis[nb] = ((mw[nb] >> (4 * q4)) & 0xfu) | (((mw[nb] >> (16 + 4 * q4)) & 0xfu) << 4);
+        vis[nb] &= in_tile;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          xs[e] = ((vis >> e) & 1u) ? st[nb][e >> 2][e & 3] : -INFINITY;
-          p[e] = fast_exp2(fmaf(xs[e], a.c, negm[nb]));
+          const uint32_t keep = (uint32_t)((int32_t)(vis[nb] << (31 - e)) >> 31);   // all ones or zero
+          p[nb][e] = __uint_as_float(__float_as_uint(fast_exp2(fmaf(st[nb][e >> 2][e & 3], a.c, negm[nb]))) & keep);
         }
-        float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        const bool need = !(ps <= P_LIMIT) || mrun[nb] == -INFINITY;
-        if (__any(need)) rescale(nb, xs, p, ps, need);
-        lrun[nb] += ps;
-        pack(nb, p);
+        ps[nb] = ((p[nb][0] + p[nb][1]) + (p[nb][2] + p[nb][3])) + ((p[nb][4] + p[nb][5]) + (p[nb][6] + p[nb][7]));
+        need[nb] = !(ps[nb] <= P_LIMIT) || mrun[nb] == -INFINITY;
+        any_need = any_need || need[nb];
       }
+      if (__builtin_expect(__any(any_need), 0)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float xs[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xs[e] = ((vis[nb] >> e) & 1u) ? st[nb][e >> 2][e & 3] : -INFINITY;
+          rescale(nb, xs, p[nb], ps[nb], need[nb]);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        lrun[nb] += ps[nb];
+        pack(nb, p[nb]);
+      }
+      // keeps this tail distinct from softmax_full's: where a branch chooses
+      // between the two, the compiler would otherwise merge the identical tails
+      // behind a choice of array addresses, which puts the arrays in scratch
+      __builtin_amdgcn_sched_barrier(0);
     };
     // segment and in-tile key count of tile t; the block rows' mask words of the lane's rows
     auto tile_kind = [&](int t, int& seg, int& lim) __attribute__((always_inline)) {
@@ -687,25 +708,29 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
           read_v(tp, vf);
         }
       };
+      // one call site each for the scores, P*V and the softmax
       if (has_t) {   // then has_p as well
+        bf16x8 kf[2][DC];
+        read_k(t, kf);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
+        scores(kf, st);
+      } else {
+#pragma unroll
+        for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      block_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_p) {
+        bf16x8 vf[DB];
+        read_pv(vf);
+        pv(vf);
+      }
+      if (has_t) {
         int seg, lim;
         tile_kind(t, seg, lim);
-        {
-          bf16x8 kf[2][DC];
-          read_k(t, kf);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
-          scores(kf, st);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        block_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        {
-          bf16x8 vf[DB];
-          read_pv(vf);
-          pv(vf);
-        }
         __builtin_amdgcn_s_setprio(1);
         if (seg == 0 && lim == C::TK) {
           softmax_full(true);
@@ -716,15 +741,6 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
-      } else {
-#pragma unroll
-        for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
-        if (has_p) {
-          bf16x8 vf[DB];
-          read_pv(vf);
-          pv(vf);
-        }
-        block_barrier();
       }
     };
     const int nfull = (ke - ks) / C::TK;
