@@ -390,6 +390,20 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         }
       }
     };
+    // S^T = K Q^T + bias (bias -inf hides a key: the score is -inf, its
+    // probability exactly 0, as with an additive -inf mask)
+    auto scores_biased = [&](const bf16x8 (&kf)[2][DC], f32x4 (&sc)[NB][2], const f32x4 (&bias)[NB][2])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          f32x4 acc = bias[nb][kb];
+#pragma unroll
+          for (int dc = 0; dc < DC; ++dc) acc = mfma16x16x32(kf[kb][dc], qf[nb][dc], acc);
+          sc[nb][kb] = acc;
+        }
+    };
     // S^T = K Q^T
     auto scores = [&](const bf16x8 (&kf)[2][DC], f32x4 (&sc)[NB][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -520,22 +534,15 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         pack(nb, p[nb]);
       }
     };
-    // softmax of a tile that needs masking: ragged prefix tail (seg 0), soft
-    // prompt (seg 1), block rows (seg 2, whose mask words the caller read: mw)
-    // A hidden key's probability is its computed value with every bit cleared
-    // (+0 whatever the slot holds, NaN included); the masked scores (-inf where
-    // hidden) are formed only when a rescale needs them.  One rescale branch
-    // for all row blocks, as in softmax_full.
-    auto softmax_masked = [&](int seg, int lim, const uint32_t (&mw)[NB]) __attribute__((always_inline)) {
-      // keys below lim: slots e < 4 hold keys 4 q4 + e, slots e >= 4 keys 16 + 4 q4 + e - 4
+    // visibility of the lane's 8 keys of a tile (bit e: slot e) for each of its
+    // rows: ragged prefix tail (seg 0), soft prompt (seg 1), block rows (seg 2,
+    // whose mask words the caller read: mw).  Keys below lim exist; slots e < 4
+    // hold tile keys 4 q4 + e, slots e >= 4 keys 16 + 4 q4 + e - 4.
+    auto visibility = [&](int seg, int lim, const uint32_t (&mw)[NB], uint32_t (&vis)[NB]) __attribute__((always_inline)) {
       const int nlo = clampi(lim - 4 * q4, 0, 4), nhi = clampi(lim - 16 - 4 * q4, 0, 4);
       const uint32_t in_tile = ((1u << nlo) - 1u) | (((1u << nhi) - 1u) << 4);
-      uint32_t vis[NB];
-      float p[NB][8], ps[NB];
-      bool need[NB], any_need = false;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        // visibility of the lane's 8 keys (tile keys 16 kb + 4 q4 + i) for its row
         if (seg == 0)
           vis[nb] = row_ok[nb] ? 0xffu : 0u;
         else if (seg == 1)
@@ -543,6 +550,20 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         else
           vis[nb] = ((mw[nb] >> (4 * q4)) & 0xfu) | (((mw[nb] >> (16 + 4 * q4)) & 0xfu) << 4);
         vis[nb] &= in_tile;
+      }
+    };
+    // softmax of a tile that needs masking (the first step's tile).  A hidden
+    // key's probability is its computed value with every bit cleared (+0
+    // whatever the slot holds, NaN included); the masked scores (-inf where
+    // hidden) are formed only when a rescale needs them.  One rescale branch
+    // for all row blocks, as in softmax_full.
+    auto softmax_masked = [&](int seg, int lim, const uint32_t (&mw)[NB]) __attribute__((always_inline)) {
+      uint32_t vis[NB];
+      visibility(seg, lim, mw, vis);
+      float p[NB][8], ps[NB];
+      bool need[NB], any_need = false;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t keep = (uint32_t)((int32_t)(vis[nb] << (31 - e)) >> 31);   // all ones or zero
@@ -570,6 +591,61 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       // between the two, the compiler would otherwise merge the identical tails
       // behind a choice of array addresses, which puts the arrays in scratch
       __builtin_amdgcn_sched_barrier(0);
+    };
+    // the additive mask of a tile's scores: +0 for a key the lane's row sees,
+    // -inf for one it does not
+    auto mask_bias = [&](int seg, int lim, const uint32_t (&mw)[NB], f32x4 (&bias)[NB][2]) __attribute__((always_inline)) {
+      uint32_t vis[NB];
+      visibility(seg, lim, mw, vis);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bias[nb][e >> 2][e & 3] = ((vis[nb] >> e) & 1u) ? 0.f : -INFINITY;
+    };
+    // softmax of a tile whose scores carry mask_bias: the unmasked arithmetic.
+    // A hidden key's score is -inf, so its probability is 0, unless its K is
+    // not finite: then the score is NaN, the tile's sum is NaN and the wave
+    // takes the branch, which redoes the tile as softmax_masked does (hidden
+    // keys selected out) -- so a hidden key's K never reaches a row, and every
+    // row gets softmax_masked's results bit for bit.
+    auto softmax_biased = [&](int seg, int lim, const uint32_t (&mw)[NB]) __attribute__((always_inline)) {
+      float p[NB][8], ps[NB];
+      bool need[NB], any_need = false;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[nb][e] = fast_exp2(fmaf(st[nb][e >> 2][e & 3], a.c, negm[nb]));
+        ps[nb] = ((p[nb][0] + p[nb][1]) + (p[nb][2] + p[nb][3])) + ((p[nb][4] + p[nb][5]) + (p[nb][6] + p[nb][7]));
+        need[nb] = mrun[nb] == -INFINITY || !(ps[nb] <= P_LIMIT);
+        any_need = any_need || need[nb];
+      }
+      if (__builtin_expect(__any(any_need), 0)) {
+        uint32_t vis[NB];
+        visibility(seg, lim, mw, vis);
+        float xs[NB][8];
+        any_need = false;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xs[nb][e] = ((vis[nb] >> e) & 1u) ? st[nb][e >> 2][e & 3] : -INFINITY;
+            p[nb][e] = fast_exp2(fmaf(xs[nb][e], a.c, negm[nb]));
+          }
+          ps[nb] = ((p[nb][0] + p[nb][1]) + (p[nb][2] + p[nb][3])) + ((p[nb][4] + p[nb][5]) + (p[nb][6] + p[nb][7]));
+          need[nb] = !(ps[nb] <= P_LIMIT) || mrun[nb] == -INFINITY;
+          any_need = any_need || need[nb];
+        }
+        if (__any(any_need)) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) rescale(nb, xs[nb], p[nb], ps[nb], need[nb]);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        lrun[nb] += ps[nb];
+        pack(nb, p[nb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // a tail of its own, as in softmax_masked
     };
     // segment and in-tile key count of tile t; the block rows' mask words of the lane's rows
     auto tile_kind = [&](int t, int& seg, int& lim) __attribute__((always_inline)) {
@@ -708,14 +784,22 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
           read_v(tp, vf);
         }
       };
-      // one call site each for the scores, P*V and the softmax
+      // The mask enters as the scores' initial accumulator, built before the
+      // hand-off while the K fragments arrive, so the softmax half -- the
+      // longer one in these steps -- runs the unmasked softmax.
+      int seg = 0, lim = 0;
+      uint32_t mw[NB];
       if (has_t) {   // then has_p as well
+        tile_kind(t, seg, lim);
+        read_mask(t, seg, mw);
         bf16x8 kf[2][DC];
         read_k(t, kf);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
-        scores(kf, st);
+        f32x4 bias[NB][2];
+        mask_bias(seg, lim, mw, bias);
+        scores_biased(kf, st, bias);
       } else {
 #pragma unroll
         for (int j = 0; j < C::LPS; ++j) issue_one(src, j);
@@ -729,17 +813,8 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         pv(vf);
       }
       if (has_t) {
-        int seg, lim;
-        tile_kind(t, seg, lim);
         __builtin_amdgcn_s_setprio(1);
-        if (seg == 0 && lim == C::TK) {
-          softmax_full(true);
-        } else {
-          uint32_t mw[NB];
-          read_mask(t, seg, mw);
-          softmax_masked(seg, lim, mw);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        softmax_biased(seg, lim, mw);
         __builtin_amdgcn_s_setprio(0);
       }
     };

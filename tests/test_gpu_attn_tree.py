@@ -274,3 +274,50 @@ def test_msa_fused_full_size():
     fo, fl, to, tl = fused_and_two_calls(st)
     assert_bitwise(fo, to, "out")
     assert_bitwise(fl, tl, "lse")
+
+
+@pytest.mark.parametrize("layout", ["bhld", "bhld_vt"])
+def test_hidden_nonfinite_keys_never_reach_a_row(layout):
+    """A key a row cannot see never reaches its output, whatever its K holds:
+    NaN and infinities in the contemplate rows' and the soft prompt's K (with
+    new finite V) leave the tree-node rows bitwise unchanged, and NaN in one
+    leaf node's K leaves every row that does not see that node bitwise unchanged
+    (rows that see it turn NaN, as the definition gives).  A hidden key's V must
+    be finite: the P*V product multiplies it by a zero probability."""
+    cfg = wl.CONFIGS["c3_confu_8b"]
+    x = wl.generate(cfg, B=2, L=(200, 231), with_logits=False)
+    T = cfg.T
+
+    def run(st):
+        st.attention_tree()
+        torch.cuda.synchronize()
+        return st.out.cpu().numpy().copy(), st.lse.cpu().numpy().copy()
+
+    st = VerifyStep(cfg, x, layout=layout)
+    base, base_lse = run(st)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    st.k_blk[:, T:] = float("nan")
+    st.v_blk[:, T:] = torch.randn(st.v_blk[:, T:].shape, generator=g, device="cuda").to(torch.bfloat16)
+    st.k_soft.fill_(float("inf"))
+    st.v_soft.copy_(torch.randn(st.v_soft.shape, generator=g, device="cuda").to(torch.bfloat16))
+    out, lse = run(st)
+    say(f"    {layout}: node rows finite after non-finite hidden K: {np.isfinite(out[:, :T]).all()}")
+    assert_bitwise(out[:, :T], base[:, :T], "node rows' outputs")
+    assert_bitwise(lse[:, :T], base_lse[:, :T], "node rows' lse")
+
+    par = x["attn_parent"][0]
+    nq = int(x["n_q"][0])
+    Tq = par.shape[0]
+    parents = {int(p) for p in par[:min(nq, T)]}                # links among the tree nodes
+    j = max(r for r in range(1, min(nq, T)) if r not in parents)   # a leaf of the node tree
+    M = oracle.block_visibility(par, nq, Tq)
+    sees = M[:, j]
+    st = VerifyStep(cfg, x, layout=layout)
+    st.k_blk[0, j] = float("nan")
+    out, lse = run(st)
+    say(f"    {layout}: leaf {j} seen by rows {np.flatnonzero(sees).tolist()}")
+    assert sees[j] and sees.sum() < nq
+    assert_bitwise(out[0, ~sees], base[0, ~sees], "rows that do not see the leaf")
+    assert_bitwise(lse[0, ~sees], base_lse[0, ~sees], "lse of rows that do not see the leaf")
+    assert np.isnan(out[0, sees]).all()
+    assert_bitwise(out[1], base[1], "the other request")
