@@ -320,7 +320,11 @@ size_t spec_verify_attn_workspace(const spec_attn_desc* d);
  *
  * Computation: fp32 accumulation; bf16 inputs use bf16 MFMA for QK^T and PV
  * (probabilities rounded to bf16 for PV); fp32 inputs use fp32 VALU
- * arithmetic throughout.  Alignment: all tensors 16-byte aligned, and
+ * arithmetic throughout.  A key a row does not see never reaches that row
+ * through its K, whatever the K holds; its V enters the P*V product times a
+ * zero probability, so the V rows of keys within [0, L_b), [0, S) and
+ * [0, n_q[b]) must be finite (cache rows past L_b are never read).
+ * Alignment: all tensors 16-byte aligned, and
  * the strides a multiple of 16 bytes.
  * Limits: D in {64, 128}; 1 <= Tq <= 256; 0 <= S <= 256; B == 0 is a no-op.
  */
