@@ -318,17 +318,15 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   // not ends the chain).  Multi-stream rows: the chain runs over the tree
   // nodes from the row's node v, and stream j of v also sees streams 1..j of
   // v (rows n + v gamma .. + j - 1).  The walk of a chain of depth d takes d
-  // dependent LDS reads; the words stay in registers.
+  // dependent LDS reads; the bits go straight into the row's words in LDS.
   if (tree && last && tid < C::ROWS) {
     const int rl = tid;
     const int r = min((row0 + rl) / a.G, a.Tq - 1);
-    uint32_t wv[C::MAXW];
-#pragma unroll
-    for (int w = 0; w < C::MAXW; ++w) wv[w] = 0u;
-    auto set_bit = [&](int c) __attribute__((always_inline)) {
-#pragma unroll
-      for (int w = 0; w < C::MAXW; ++w) wv[w] |= (c >> 5) == w ? 1u << (c & 31) : 0u;
-    };
+    uint32_t* const words = mask_lds + rl * a.W;   // this thread's row alone
+    for (int w = 0; w < a.W; ++w) words[w] = 0u;
+    // one LDS OR per key, issued without waiting: a chain step costs one
+    // dependent LDS read
+    auto set_bits = [&](int w, uint32_t bits) __attribute__((always_inline)) { atomicOr(words + w, bits); };
     if (r < nq) {
       int cur = r, j = 0;
       if (msa && r >= msa_n) {
@@ -336,21 +334,19 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
         j = (r - msa_n) % a.msa_gamma + 1;
       }
       const int node = cur;
-      set_bit(cur);
+      set_bits(cur >> 5, 1u << (cur & 31));
       for (int pr = par_l[cur]; pr >= 0 && pr < cur; pr = par_l[pr]) {
-        set_bit(pr);
+        set_bits(pr >> 5, 1u << (pr & 31));
         cur = pr;
       }
-      if (j > 0) {
+      if (j > 0) {   // streams 1..j of the node: rows s0 .. s0 + j - 1
         const int s0 = msa_n + node * a.msa_gamma;
-#pragma unroll
-        for (int w = 0; w < C::MAXW; ++w) {
+        for (int w = s0 >> 5; w <= (s0 + j - 1) >> 5; ++w) {
           const int lo = max(s0, 32 * w), hi = min(s0 + j, 32 * w + 32);
-          if (lo < hi) wv[w] |= (hi - lo == 32 ? ~0u : ((1u << (hi - lo)) - 1u)) << (lo - 32 * w);
+          set_bits(w, (hi - lo == 32 ? ~0u : ((1u << (hi - lo)) - 1u)) << (lo - 32 * w));
         }
       }
     }
-    for (int w = 0; w < a.W; ++w) mask_lds[rl * a.W + w] = wv[w];
   }
   // the staged queries are overwritten by step P/2's V loads, issued only after
   // a barrier that every wave reaches after this; the mask words are read after
