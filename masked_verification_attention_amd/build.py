@@ -25,12 +25,15 @@ SOURCES = ["api.hip", "mask.hip", "attn_valu.hip", "attn_mfma.hip", "accept.hip"
 ARCH = os.environ.get("SPEC_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU ops are disabled for device code (hipcc's host pass warns
-# that it does not know the feature; that is harmless).
+# that it does not know the feature; that is harmless).  Loop heads start on
+# 64-byte boundaries, so the attention's hot loop does not move within an
+# instruction-cache line when unrelated code changes (its time had swung by a
+# few percent with such moves).
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Werror",
     "-Wno-unused-function", "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics",
+    "-munsafe-fp-atomics", "-falign-loops=64",
 ]
 
 
