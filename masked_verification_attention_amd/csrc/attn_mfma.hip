@@ -74,18 +74,50 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   __shared__ uint32_t sp_lds[64];                      // the request's soft-prompt words
 
   // ---- which (split, request, kv-head, row chunk): siblings of a row chunk
-  // sit on the same XCD (workgroups are dealt round-robin over 8 XCDs)
+  // sit on the same XCD (workgroups are dealt round-robin over 8 XCDs: XCD x
+  // runs workgroups x, x + 8, ... in order, each on the first CU that frees)
   const int nwg = gridDim.x;
   const int bid = blockIdx.x;
-  const int item = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
-  const int chunk_id = item % a.row_chunks;
-  const int rest = item / a.row_chunks;
-  const int bh = rest % (a.B * a.Hkv);
-  const int split = rest / (a.B * a.Hkv);
-  const int b = bh / a.Hkv;
-  const int h = bh % a.Hkv;
-
   const int tid = threadIdx.x;
+  int chunk_id, split, b, h;
+  if (a.balance) {
+    // A grid of several rounds finishes when its last workgroup does: the
+    // pairs go longest prefix first, pair of rank k to XCD k mod 8, so every
+    // XCD gets a share of the long ones and ends on short ones.  The rank of
+    // a request: the requests with a longer prefix, or as long and a lower
+    // index, before it.  The lengths pass through the start of the ring, which
+    // nothing loads into before the barrier that ends this.
+    __shared__ int pick;
+    const int q = bid / 8;
+    const int k = (q / a.row_chunks) * 8 + bid % 8;   // the pair's rank
+    chunk_id = q % a.row_chunks;
+    split = 0;
+    h = k % a.Hkv;
+    const int r = k / a.Hkv;
+    int* const lens = reinterpret_cast<int*>(ring);
+    for (int j = tid; j < a.B; j += C::kThreads) lens[j] = (int)min<int64_t>(max(a.cache_len[j], 0), a.lmax);
+    __syncthreads();
+    for (int j = tid; j < a.B; j += C::kThreads) {
+      const int lj = lens[j];
+      int rk = 0;
+      for (int i = 0; i < a.B; ++i) {
+        const int li = lens[i];
+        rk += (li > lj || (li == lj && i < j)) ? 1 : 0;
+      }
+      if (rk == r) pick = j;
+    }
+    __syncthreads();
+    b = pick;
+  } else {
+    const int item = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+    chunk_id = item % a.row_chunks;
+    const int rest = item / a.row_chunks;
+    const int bh = rest % (a.B * a.Hkv);
+    split = rest / (a.B * a.Hkv);
+    b = bh / a.Hkv;
+    h = bh % a.Hkv;
+  }
+
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int grp = wave >> 2;          // key-tile parity this wave computes
   const int wq = wave & 3;            // row slice within the workgroup
@@ -893,9 +925,14 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   }
 }
 
-hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
-  const int64_t nwg = (int64_t)a.n_split * a.row_chunks * a.B * a.Hkv;
+hipError_t launch_attn_mfma(const AttnArgs& args, hipStream_t st) {
+  const int64_t nwg = (int64_t)args.n_split * args.row_chunks * args.B * args.Hkv;
   const dim3 grid((unsigned)nwg);
+  // longest-first dealing once the grid takes more than one round of
+  // workgroups (256 CUs; two 64-row head-dim-64 workgroups fit in one CU)
+  AttnArgs a = args;
+  const int per_cu = a.D == 64 ? 2 : 1;
+  a.balance = a.n_split == 1 && (int64_t)a.B * a.Hkv % 8 == 0 && a.B <= 4096 && nwg > 256 * per_cu;
   const dim3 block(512);
   auto go = [&](auto vt) -> hipError_t {
     constexpr bool VT = decltype(vt)::value;

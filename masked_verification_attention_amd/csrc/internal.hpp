@@ -48,6 +48,10 @@ struct AttnArgs {
   const uint8_t* sp_flag;           // [B][Tq] or NULL (MASK_PARENT)
   const int32_t* n_nodes;           // [B] (MASK_MSA)
   int msa_N, msa_gamma;
+  // MFMA path: deal the (request, kv-head) pairs over the XCDs longest prefix
+  // first (set by the launcher when the grid takes more than one round of
+  // workgroups; needs n_split == 1 and B * Hkv a multiple of 8)
+  int balance;
 };
 
 enum MaskMode { MASK_WORDS = 0, MASK_PARENT = 1, MASK_MSA = 2 };
