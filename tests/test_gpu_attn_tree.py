@@ -321,3 +321,30 @@ def test_hidden_nonfinite_keys_never_reach_a_row(layout):
     assert_bitwise(lse[0, ~sees], base_lse[0, ~sees], "lse of rows that do not see the leaf")
     assert np.isnan(out[0, sees]).all()
     assert_bitwise(out[1], base[1], "the other request")
+
+
+def test_longest_first_dealing_covers_every_row():
+    """A grid of several rounds (32 requests x 8 kv-heads x 3 row chunks) with
+    ragged prefixes takes the longest-first dealing of pairs over the XCDs:
+    every valid row is written (NaN-filled output, all finite afterwards),
+    padded rows are zero, and the longest, the shortest and two middle requests
+    match the oracle."""
+    cfg = wl.CONFIGS["c4_tree_3b"]
+    x = wl.generate(cfg, L=(64, 1500), with_logits=False)
+    assert x["q"].shape[0] * cfg.Hkv % 8 == 0
+    st = VerifyStep(cfg, x, layout="bhld")
+    st.out.fill_(float("nan"))
+    st.lse.fill_(float("nan"))
+    st.attention_tree()
+    torch.cuda.synchronize()
+    out, lse = st.out.cpu().numpy(), st.lse.cpu().numpy()
+    for b in range(out.shape[0]):
+        nq = int(x["n_q"][b])
+        assert np.isfinite(out[b, :nq]).all() and np.isfinite(lse[b, :nq]).all(), f"request {b}"
+        assert (out[b, nq:] == 0).all() and np.isneginf(lse[b, nq:]).all(), f"request {b} padding"
+    order = np.argsort(-x["cache_len"], kind="stable")
+    pick = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), int(order[len(order) // 3])})
+    say(f"    prefixes {int(x['cache_len'].min())}..{int(x['cache_len'].max())}; oracle on requests {pick}")
+    sub = {k: (v[pick] if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == out.shape[0] else v)
+           for k, v in x.items()}
+    check_oracle(out[pick], lse[pick], sub, cfg)
