@@ -354,14 +354,13 @@ __device__ __forceinline__ bool key_less(uint64_t ah, uint64_t al, uint64_t bh, 
 
 // LDS of one request's acceptance scan
 struct AcceptSmem {
-  int32_t par[SPEC_MAX_NODES];
-  uint8_t okv[SPEC_MAX_NODES];
+  int32_t link[SPEC_MAX_NODES];   // the node's parent if it is accepted, else INT_MIN
+  int32_t gbon[SPEC_MAX_NODES];   // the greedy token of the node's own row (correction token)
   float row_lse[SPEC_MAX_NODES];
   int32_t path_s[SPEC_MAX_DEPTH];
   int red_i[kAccThreads / kWave];
   uint64_t red_h[kAccThreads / kWave];
   uint64_t red_l[kAccThreads / kWave];
-  uint8_t lists[kAccThreads][SPEC_MAX_DEPTH];
 };
 
 // The acceptance scan (and, when enabled, the commit) of request b by one
@@ -376,7 +375,8 @@ __device__ __forceinline__ void accept_request(AcceptSmem& sm, int b, int T_, co
   const int lane = v % kWave;
   // Every load that does not depend on another goes out first, in one round
   // trip: the node count, the cache length the commit appends at, and the
-  // node's parent, draft and (for its own row) greedy token.
+  // node's parent, draft and own row's greedy token (the acceptance test, or
+  // the correction token should the node end the path).
   const int n = clampi(n_nodes[b], 0, T_);
   const int64_t len_in = commit.enabled ? commit.cache_len_in[b] : 0;
   int par_v = -1, x = -1, u = v, g_own = -1;
@@ -384,20 +384,21 @@ __device__ __forceinline__ void accept_request(AcceptSmem& sm, int b, int T_, co
     par_v = acc_parent[(int64_t)b * T_ + v];
     x = draft_tok[(int64_t)b * T_ + v];
     if (verify_row) u = verify_row[(int64_t)b * T_ + v];
-    else if (rule.mode == 0) g_own = argmax[(int64_t)b * T_ + v];
+    if ((rule.mode == 0 && !verify_row) || out_bonus != nullptr) g_own = argmax[(int64_t)b * T_ + v];
   }
   // probability rules: every row's log-sum-exp is staged before the same
   // buffer receives the nodes' probabilities
   if (rule.mode != 0 && v < n) sm.row_lse[v] = rule.prob[(int64_t)b * T_ + v];
   __syncthreads();
   if (v < n) {
-    sm.par[v] = par_v;
+    sm.gbon[v] = g_own;
     // the row that verifies node v: v itself, or the given row (-1 = accepted
     // unchecked; a row outside [0, n) never accepts)
     const bool in_rows = u >= 0 && u < n;
+    bool okv;
     if (rule.mode == 0) {
       const int g = verify_row ? (in_rows ? argmax[(int64_t)b * T_ + u] : -1) : g_own;
-      sm.okv[v] = u == -1 ? 1 : ((in_rows && x == g) ? 1 : 0);
+      okv = u == -1 || (in_rows && x == g);
     } else {
       // target probability of the draft at its row: exp(logit - lse)
       float p = u == -1 ? 1.f : 0.f;
@@ -407,36 +408,38 @@ __device__ __forceinline__ void accept_request(AcceptSmem& sm, int b, int T_, co
                                          : static_cast<const float*>(rule.logits)[at];
         p = fast_exp2((l - sm.row_lse[u]) * 1.4426950408889634f);
       }
-      bool ok;
-      if (u == -1) ok = true;
-      else if (!in_rows) ok = false;
-      else if (rule.mode == 1) ok = p > rule.threshold;
-      else ok = rule.uniform[(int64_t)b * T_ + v] * rule.draft_prob[(int64_t)b * T_ + v] < p;
-      sm.okv[v] = ok ? 1 : 0;
+      if (u == -1) okv = true;
+      else if (!in_rows) okv = false;
+      else if (rule.mode == 1) okv = p > rule.threshold;
+      else okv = rule.uniform[(int64_t)b * T_ + v] * rule.draft_prob[(int64_t)b * T_ + v] < p;
       rule.prob[(int64_t)b * T_ + v] = p;
     }
+    // a rejected node's link is INT_MIN, which ends a walk as a broken link does
+    sm.link[v] = okv ? par_v : INT_MIN;
   }
   __syncthreads();
 
-  // walk to the root; list[] holds the path bottom-up
+  // Walk to the root, one LDS read per level (the node's link).  The path's
+  // nodes go into a 128-bit key, 8 bits each, shifted in from the top as the
+  // walk climbs: when it ends at the root, the root is the top byte and the
+  // walk's first node the lowest used one -- the root-first path, compared as
+  // a number below.  Unused bytes are 0.
   int depth = 0;
   bool acc = false;
-  uint8_t* list = sm.lists[v];
+  uint64_t ph = 0ull, pl = 0ull;
   if (v < n) {
     int cur = v;
     bool good = true;
     while (cur >= 0) {
-      if (depth >= max_depth || !sm.okv[cur]) {
+      const int l = sm.link[cur];
+      if (depth >= max_depth || l < -1 || l >= cur) {   // rejected, or a broken link
         good = false;
         break;
       }
-      list[depth++] = (uint8_t)cur;
-      const int p = sm.par[cur];
-      if (p < -1 || p >= cur) {   // broken link: not a path to the root
-        good = false;
-        break;
-      }
-      cur = p;
+      pl = (pl >> 8) | (ph << 56);
+      ph = (ph >> 8) | ((uint64_t)cur << 56);
+      ++depth;
+      cur = l;
     }
     acc = good;
   }
@@ -453,13 +456,8 @@ __device__ __forceinline__ void accept_request(AcceptSmem& sm, int b, int T_, co
   // lexicographically smallest root-first path among accepted nodes of depth A
   uint64_t kh = ~0ull, kl = ~0ull;
   if (acc && depth == a_len && a_len > 0) {
-    kh = 0ull;
-    kl = 0ull;
-    for (int d = 0; d < depth; ++d) {
-      const uint64_t node = (uint64_t)list[depth - 1 - d];
-      if (d < 8) kh |= node << (56 - 8 * d);
-      else kl |= node << (56 - 8 * (d - 8));
-    }
+    kh = ph;
+    kl = pl;
   }
   uint32_t kw[4] = {(uint32_t)kh, (uint32_t)(kh >> 32), (uint32_t)kl, (uint32_t)(kl >> 32)};
   wave_allreduce<4>(kw, [](uint32_t (&x)[4], const uint32_t (&y)[4]) {
@@ -496,7 +494,7 @@ __device__ __forceinline__ void accept_request(AcceptSmem& sm, int b, int T_, co
         const int d = a_len - 1;
         const uint64_t w = d < 8 ? kh : kl;
         const int last = (int)((w >> (56 - 8 * (d & 7))) & 0xffull);
-        bonus = argmax[(int64_t)b * T_ + last];
+        bonus = sm.gbon[last];
       }
       out_bonus[b] = bonus;
     }
