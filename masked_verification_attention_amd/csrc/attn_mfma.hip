@@ -793,11 +793,10 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       __builtin_amdgcn_s_setprio(0);
     };
     // A step after the hot ones (its own tile, if any, is a ragged prefix, soft
-    // or block tile; its P*V tile may be too).  The hot step's schedule for the
-    // scores -- K fragments first, the hand-off barrier after 12 matrix
-    // instructions -- with the V fragments read only once the K fragments are
-    // dead (both at once would overflow the registers here), then P*V and the
-    // masked softmax.
+    // or block tile; its P*V tile may be too).  K fragments first, then the
+    // step's loads, the scores and the hand-off barrier; the V fragments are
+    // read only once the K fragments are dead (both at once would overflow the
+    // registers here), then P*V and the softmax.
     auto tail_step = [&](int s) __attribute__((always_inline)) {
       begin_step(s);
       const TileSrc src = tile_src(s + C::P / 2);
