@@ -20,7 +20,9 @@
 // reduction over the lists.  Ties resolve to the lower token index; -0 equals +0; NaN ranks
 // after every number (lowest index first among NaNs).
 //
-// k_draft_tree: one workgroup per request writes tokens and parents.
+// Each top-k workgroup then writes its stream's level of the next tree
+// (tokens and parents); k_draft_tree, one workgroup per request, writes the
+// tree only when it is the root alone (gamma = 0).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -192,7 +194,8 @@ template <typename T>
 __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
     const T* __restrict__ logits, int R, int V, const int32_t* __restrict__ n_nodes,
     const int32_t* __restrict__ acc_len, const int32_t* __restrict__ acc_path, int max_depth, int gamma,
-    int k, int32_t* __restrict__ out_topk) {
+    int k, int32_t* __restrict__ out_topk, int N, const int32_t* __restrict__ root_tok,
+    int32_t* __restrict__ draft_tok, int32_t* __restrict__ tree_parent, int32_t* __restrict__ n_out) {
   constexpr int K = SPEC_MAX_TOPK;
   constexpr int U = 8;        // loads in flight per thread
   constexpr int kCap = 256;   // candidates ranked directly; more go through the list merge
@@ -203,16 +206,41 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
   __shared__ int cand_i[kCap];
   __shared__ float bound_s;
   __shared__ int cnt_s, nan_s;
+  __shared__ int tk_s[K];
   const int b = blockIdx.x / gamma;
   const int j = blockIdx.x % gamma;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   int32_t* dst = out_topk + ((int64_t)b * gamma + j) * k;
+  // This workgroup also writes level j + 1 of the next tree, whose k^(j+1)
+  // nodes are the children of level j in order: node v is the ((v-1) % k)-th
+  // child of node (v-1) / k, and its token is stream j's token of that rank.
+  // Stream 0's workgroup writes the root and the node count.
+  int first = 1, cnt = k;
+  for (int g = 0; g < j; ++g) {
+    first += cnt;
+    cnt *= k;
+  }
+  int32_t* const tok_b = draft_tok + (int64_t)b * N;
+  int32_t* const par_b = tree_parent + (int64_t)b * N;
   const int row0 = root_stream_row(b, R, gamma, n_nodes, acc_len, acc_path, max_depth);
-  if (row0 < 0) {   // uniform over the workgroup
+  if (row0 < 0) {   // uniform over the workgroup: no new root, no tree
     if (tid < k) dst[tid] = -1;
+    for (int t = tid; t < cnt; t += kTopThreads) {
+      tok_b[first + t] = -1;
+      par_b[first + t] = -1;
+    }
+    if (j == 0 && tid == 0) {
+      tok_b[0] = -1;
+      par_b[0] = -1;
+      n_out[b] = 0;
+    }
     return;
   }
+  auto put = [&](int r, int tok) __attribute__((always_inline)) {
+    dst[r] = tok;
+    tk_s[r] = tok;
+  };
   const T* base = logits + ((int64_t)b * R + row0 + j) * V;
 
   // pass 1: the largest value of each wave (NaN ignored).  The k-th largest
@@ -272,7 +300,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
       const int ci = cand_i[tid];
       int rank = 0;
       for (int c = 0; c < n; ++c) rank += ranks_before(cand_v[c], cand_i[c], cv, ci) ? 1 : 0;
-      if (rank < k) dst[rank] = ci;
+      if (rank < k) put(rank, ci);
     }
     // Fewer than k numbers in the row (the bound is then -inf and every
     // number is a candidate): NaN entries follow every number, lowest index
@@ -289,7 +317,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
       __syncthreads();
       const int got = nan_s;
       __syncthreads();
-      if (tid == 0) dst[r] = got == 0x7fffffff ? -1 : got;
+      if (tid == 0) put(r, got == 0x7fffffff ? -1 : got);
       prev = got;
     }
   } else {
@@ -299,8 +327,19 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_streams(
     if (tid == 0) {
 #pragma unroll
       for (int r = 0; r < K; ++r)
-        if (r < k) dst[r] = oi[r] == 0x7fffffff ? -1 : oi[r];
+        if (r < k) put(r, oi[r] == 0x7fffffff ? -1 : oi[r]);
     }
+  }
+  __syncthreads();
+  for (int t = tid; t < cnt; t += kTopThreads) {
+    const int v = first + t;
+    tok_b[v] = tk_s[(v - 1) % k];
+    par_b[v] = (v - 1) / k;
+  }
+  if (j == 0 && tid == 0) {
+    tok_b[0] = root_tok[b];
+    par_b[0] = -1;
+    n_out[b] = N;
   }
 }
 
@@ -343,20 +382,21 @@ hipError_t launch_draft_tree(const void* logits, int dtype, int B, int R, int V,
                              const int32_t* acc_len, const int32_t* acc_path, int max_depth,
                              const int32_t* root_tok, int gamma, int k, int N, int32_t* out_topk,
                              int32_t* draft_tok, int32_t* tree_parent, int32_t* n_out, hipStream_t st) {
-  if (gamma > 0) {
-    const dim3 grid((unsigned)((int64_t)B * gamma));
-    if (dtype == SPEC_BF16)
-      hipLaunchKernelGGL(k_topk_streams<uint16_t>, grid, dim3(kTopThreads), 0, st,
-                         static_cast<const uint16_t*>(logits), R, V, n_nodes, acc_len, acc_path, max_depth, gamma,
-                         k, out_topk);
-    else
-      hipLaunchKernelGGL(k_topk_streams<float>, grid, dim3(kTopThreads), 0, st, static_cast<const float*>(logits),
-                         R, V, n_nodes, acc_len, acc_path, max_depth, gamma, k, out_topk);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (gamma == 0) {   // the tree is the root alone
+    hipLaunchKernelGGL(k_draft_tree, dim3(B), dim3(256), 0, st, R, gamma, k, N, n_nodes, acc_len, acc_path,
+                       max_depth, root_tok, out_topk, draft_tok, tree_parent, n_out);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_draft_tree, dim3(B), dim3(256), 0, st, R, gamma, k, N, n_nodes, acc_len, acc_path,
-                     max_depth, root_tok, out_topk, draft_tok, tree_parent, n_out);
+  // the top-k workgroups write the tree as well (one level each)
+  const dim3 grid((unsigned)((int64_t)B * gamma));
+  if (dtype == SPEC_BF16)
+    hipLaunchKernelGGL(k_topk_streams<uint16_t>, grid, dim3(kTopThreads), 0, st,
+                       static_cast<const uint16_t*>(logits), R, V, n_nodes, acc_len, acc_path, max_depth, gamma, k,
+                       out_topk, N, root_tok, draft_tok, tree_parent, n_out);
+  else
+    hipLaunchKernelGGL(k_topk_streams<float>, grid, dim3(kTopThreads), 0, st, static_cast<const float*>(logits), R,
+                       V, n_nodes, acc_len, acc_path, max_depth, gamma, k, out_topk, N, root_tok, draft_tok,
+                       tree_parent, n_out);
   return hipGetLastError();
 }
 
