@@ -88,14 +88,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def counters_file(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"attn_mfma_{workload}_counters.json")
+def counters_file(workload: str, out: str = "f32") -> str:
+    tag = "" if out == "f32" else f"_{out}out"
+    return os.path.join(ROOT, "profiles", f"attn_mfma_{workload}{tag}_counters.json")
 
 
-def attention_algorithmic_bytes(cfg, x, fused_mask=False) -> int:
+def attention_algorithmic_bytes(cfg, x, fused_mask=False, out_es=4) -> int:
     """Bytes the attention must move at least once: KV prefix read, soft prompt,
     queries, block K/V, mask words (or, when the launch builds the mask itself,
-    the parent array and soft-prompt flags) and the fp32 output (+ lse)."""
+    the parent array and soft-prompt flags) and the output (``out_es`` bytes a
+    value: fp32 or bf16) with its fp32 lse."""
     es = 2 if cfg.dtype == "bf16" else 4
     B, Tq = x["q"].shape[:2]
     W = (Tq + 31) // 32
@@ -104,7 +106,7 @@ def attention_algorithmic_bytes(cfg, x, fused_mask=False) -> int:
     q = B * Tq * cfg.Hq * cfg.D * es
     blk = B * Tq * cfg.Hkv * cfg.D * 2 * es
     mask = B * Tq * 5 if fused_mask else B * Tq * W * 4 + B * W * 4
-    out = B * Tq * cfg.Hq * cfg.D * 4 + B * Tq * cfg.Hq * 4
+    out = B * Tq * cfg.Hq * cfg.D * out_es + B * Tq * cfg.Hq * 4
     return kv + soft + q + blk + mask + out
 
 
@@ -142,7 +144,7 @@ def argmax_bytes(cfg, x) -> int:
     return int(x["n_nodes"].sum()) * x["logits"].shape[2] * es
 
 
-def summarize_pmc(d: str, workload: str = WORKLOAD, out: str = None):
+def summarize_pmc(d: str, workload: str = WORKLOAD, out: str = None, out_dtype: str = "f32"):
     """Per-launch HBM traffic of the attention kernel from rocprofv3 counter CSVs in d
     (a FETCH_SIZE run and a WRITE_SIZE run of `bench.py --calibrate-copy`)."""
     import csv
@@ -175,7 +177,7 @@ def summarize_pmc(d: str, workload: str = WORKLOAD, out: str = None):
     fetch = mean[("attn", "FETCH_SIZE")] * 1024 * f_fetch
     write = mean[("attn", "WRITE_SIZE")] * 1024 * f_write
     rec = {
-        "kernel": "k_attn_mfma", "workload": workload,
+        "kernel": "k_attn_mfma", "workload": workload, "out": out_dtype,
         "kernel_src_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
         "taken": time.strftime("%Y-%m-%d"),
         "fetch_size_kib_per_launch": mean[("attn", "FETCH_SIZE")],
@@ -185,20 +187,22 @@ def summarize_pmc(d: str, workload: str = WORKLOAD, out: str = None):
         "traffic_bytes_per_launch": fetch + write,
         "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
     }
-    with open(out or counters_file(workload), "w") as f:
+    with open(out or counters_file(workload, out_dtype), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
 
 
-def counters_traffic(workload: str):
+def counters_traffic(workload: str, out: str = "f32"):
     """(HBM bytes per attention launch, source record) from committed rocprofv3 counter
-    runs, or (None, None) if there are none or the kernel source changed since."""
-    path = counters_file(workload)
+    runs, or (None, None) if there are none, they were taken with another output
+    dtype, or the kernel source changed since."""
+    path = counters_file(workload, out)
     try:
         with open(path) as f:
             rec = json.load(f)
         sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if rec.get("kernel_src_sha256") != sha or rec.get("workload") != workload:
+        if (rec.get("kernel_src_sha256") != sha or rec.get("workload") != workload
+                or rec.get("out", "f32") != out):
             return None, None
         src = {"file": os.path.relpath(path, ROOT), "kernel_src_sha256": sha, "taken": rec.get("taken")}
         return rec.get("traffic_bytes_per_launch"), src
@@ -338,6 +342,8 @@ def main():
                     help="block mask built inside the attention launch (spec_verify_attn_tree, where it "
                          "applies: bf16, parent-array masks) or by spec_build_mask first")
     ap.add_argument("--layout", choices=("bhld", "blhd", "bhld_vt"), default="bhld")
+    ap.add_argument("--out", choices=("f32", "bf16"), default="f32",
+                    help="attention output dtype (bf16: bf16 workloads only, the fp32 result rounded)")
     ap.add_argument("--instrumented-steps", type=int, default=0,
                     help="steps of the second pass with events around every call (0: max(steps, 100))")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -347,7 +353,7 @@ def main():
                          "write the traffic record of --workload and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, args.workload)
+        summarize_pmc(args.summarize_pmc, args.workload, out_dtype=args.out)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -365,6 +371,8 @@ def main():
     cfg = wl.CONFIGS[args.workload]
     desc, seq_len, bound = DESCRIPTIONS[args.workload]
     layout = args.layout if cfg.dtype == "bf16" or args.layout != "bhld_vt" else "bhld"
+    if args.out == "bf16" and cfg.dtype != "bf16":
+        raise SystemExit(f"--out bf16 needs a bf16 workload ({args.workload} is {cfg.dtype})")
     ceilings = None if args.no_ceilings else measured_ceilings(torch)
     if ceilings:
         log(f"measured ceilings: read {ceilings['hbm_read_gbs']:.0f} GB/s, bf16 matrix "
@@ -385,14 +393,14 @@ def main():
                         accept=args.accept, threshold=1e-3,
                         draft_prob=urng.random((cfg.B, T_acc)).astype(np.float32) * 0.02,
                         uniform=urng.random((cfg.B, T_acc)).astype(np.float32),
-                        fused_mask=None if args.mask == "fused" else False)
+                        fused_mask=None if args.mask == "fused" else False, out_dtype=args.out)
         steps_state.append((st, x))
     torch.cuda.synchronize()
     log(f"inputs: {args.sets} sets generated and uploaded in {time.time() - t0:.1f}s")
     x0 = steps_state[0][1]
     tokens_per_step = int(x0["n_q"].sum())
     fused = steps_state[0][0].fused_mask
-    alg_bytes = attention_algorithmic_bytes(cfg, x0, fused_mask=fused)
+    alg_bytes = attention_algorithmic_bytes(cfg, x0, fused_mask=fused, out_es=2 if args.out == "bf16" else 4)
     flops = attention_flops(cfg, x0)
     am_bytes = argmax_bytes(cfg, x0)
 
@@ -477,7 +485,7 @@ def main():
         f"{'mask in the attention launch' if fused else f'mask {np.mean(t_mask):.1f} us'}, "
         f"tail {tail_mean:.1f} us")
 
-    traffic, traffic_src = counters_traffic(args.workload)
+    traffic, traffic_src = counters_traffic(args.workload, args.out)
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / MFMA_BF16_PEAK_TFLOPS}
@@ -533,7 +541,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": desc, "name": args.workload, "global_batch": cfg.B, "seq_len": seq_len,
-                   "query_rows": cfg.Tq, "kv_layout": layout, "acceptance": args.accept,
+                   "query_rows": cfg.Tq, "kv_layout": layout, "acceptance": args.accept, "attn_out": args.out,
                    "input_sets": args.sets, "parallelism": "single GPU"},
         "roofline": roof,
         "step_kernels": step_kernels,

@@ -116,6 +116,9 @@ typedef struct {
   int32_t kv_splits; /* 0 = automatic; else split each request's prefix into
                         this many key ranges (tuning and testing)             */
   int32_t v_layout;  /* spec_v_layout of v_cache (K always uses the strides)  */
+  int32_t out_dtype; /* spec_dtype of out: SPEC_F32 (0, the default) or
+                        SPEC_BF16 (bf16 inputs only): each output value is the
+                        float32 result rounded to nearest even             */
 } spec_attn_desc;
 
 /* Layout of the V cache (spec_attn_desc.v_layout).
@@ -312,7 +315,7 @@ size_t spec_verify_attn_workspace(const spec_attn_desc* d);
  *   mask_bits [B, Tq, W], sp_bits [B, W] as produced by spec_build_mask
  *            (sp_bits may be NULL iff S == 0)
  *   n_q      [B] int32, clamped to [0, Tq]
- *   out      [B, Tq, Hq, D] float32
+ *   out      [B, Tq, Hq, D] float32, or bf16 when d->out_dtype is SPEC_BF16
  *   lse      [B, Tq, Hq] float32, or NULL
  *   workspace  device buffer of at least spec_verify_attn_workspace(d)
  *            bytes (may be NULL when that is 0).  Contents need no
@@ -333,7 +336,7 @@ int spec_verify_attn(const spec_attn_desc* d, const void* q,
                      const void* k_blk, const void* v_blk,
                      const void* k_soft, const void* v_soft,
                      const uint32_t* mask_bits, const uint32_t* sp_bits, const int32_t* n_q,
-                     float* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream);
 
 /*
@@ -362,7 +365,7 @@ int spec_verify_attn_tree(const spec_attn_desc* d, const void* q,
                           const void* k_blk, const void* v_blk,
                           const void* k_soft, const void* v_soft,
                           const int32_t* attn_parent, const uint8_t* sp_flag, const int32_t* n_q,
-                          float* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
 
 /*
@@ -394,7 +397,7 @@ int spec_verify_attn_msa(const spec_attn_desc* d, const void* q,
                          const void* k_blk, const void* v_blk,
                          const void* k_soft, const void* v_soft,
                          const int32_t* tree_parent, const int32_t* n_nodes, int32_t N, int32_t gamma,
-                         float* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* out, float* lse, void* workspace, size_t workspace_bytes,
                          void* stream);
 
 /*
@@ -426,7 +429,7 @@ int spec_verify_attn_noalloc(const spec_attn_desc* d, const void* q,
                              const void* k_blk, const void* v_blk,
                              const void* k_soft, const void* v_soft,
                              const uint32_t* mask_bits, const uint32_t* sp_bits, const int32_t* n_q,
-                             float* out, float* lse, void* stream);
+                             void* out, float* lse, void* stream);
 
 /*
  * spec_argmax_accept -- greedy verification of a draft tree.

@@ -56,6 +56,7 @@ class AttnDesc(ctypes.Structure):
         ("D", ctypes.c_int32), ("S", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
         ("lmax", ctypes.c_int64), ("kv_stride_b", ctypes.c_int64), ("kv_stride_l", ctypes.c_int64),
         ("kv_stride_h", ctypes.c_int64), ("kv_splits", ctypes.c_int32), ("v_layout", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
     ]
 
 
@@ -174,9 +175,10 @@ class Prepared:
             _check(status, self.name)
 
 
-def make_desc(B, Tq, Hq, Hkv, D, S, dtype, lmax, strides, scale=0.0, kv_splits=0, v_layout=SPEC_V_ROWS) -> AttnDesc:
+def make_desc(B, Tq, Hq, Hkv, D, S, dtype, lmax, strides, scale=0.0, kv_splits=0, v_layout=SPEC_V_ROWS,
+              out_dtype=SPEC_F32) -> AttnDesc:
     sb, sl, sh = strides
-    return AttnDesc(B, Tq, Hq, Hkv, D, S, dtype, scale, lmax, sb, sl, sh, kv_splits, v_layout)
+    return AttnDesc(B, Tq, Hq, Hkv, D, S, dtype, scale, lmax, sb, sl, sh, kv_splits, v_layout, out_dtype)
 
 
 def spec_build_mask(attn_parent, sp_flag, n_q, B, Tq, mask_bits, sp_bits, stream=None):

@@ -81,6 +81,10 @@ int check_desc(const spec_attn_desc* d) {
             (long long)d->lmax);
   }
   REQUIRE(isfinite(d->scale) && d->scale >= 0.f, SPEC_EINVAL, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  REQUIRE(d->out_dtype == SPEC_F32 || d->out_dtype == SPEC_BF16, SPEC_EINVAL, "out_dtype = %d is not a spec_dtype",
+          d->out_dtype);
+  REQUIRE(d->out_dtype == SPEC_F32 || d->dtype == SPEC_BF16, SPEC_EUNSUPPORTED,
+          "out_dtype SPEC_BF16 needs bf16 inputs");
   REQUIRE((int64_t)d->B * d->Hkv <= 65535, SPEC_EUNSUPPORTED, "B * Hkv = %lld exceeds 65535",
           (long long)((int64_t)d->B * d->Hkv));
   return SPEC_OK;
@@ -176,7 +180,7 @@ int argmax_accept_impl(const char* fn, const void* logits, int32_t logits_dtype,
 
 extern "C" {
 
-const char* spec_version(void) { return "0.1.0"; }
+const char* spec_version(void) { return "0.2.0"; }
 
 const char* spec_last_error(void) { return g_last_error; }
 
@@ -321,7 +325,7 @@ namespace {
 int check_attn_args(const char* fn, const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
                     const void* v_soft, const void* mask_bits, const void* sp_bits, const int32_t* n_q,
-                    const float* out, const float* lse, bool tree = false) {
+                    const void* out, const float* lse, bool tree = false) {
   const int st = check_desc(d);
   if (st != SPEC_OK) return st;
   if (d->B == 0) return SPEC_OK;
@@ -363,7 +367,7 @@ struct MaskSource {
 int launch_verify_attn(const spec_attn_desc* d, const sv::AttnPlan& plan, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* cache_len, const void* k_blk, const void* v_blk,
                        const void* k_soft, const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
-                       const int32_t* n_q, float* out, float* lse, void* workspace, void* stream,
+                       const int32_t* n_q, void* out, float* lse, void* workspace, void* stream,
                        const MaskSource& ms = MaskSource()) {
   sv::AttnArgs a{};
   a.B = d->B;
@@ -393,6 +397,7 @@ int launch_verify_attn(const spec_attn_desc* d, const sv::AttnPlan& plan, const 
   a.sp_bits = sp_bits;
   a.n_q = n_q;
   a.out = out;
+  a.out_bf16 = d->out_dtype == SPEC_BF16;
   a.lse = lse;
   a.n_split = plan.n_split;
   a.row_chunks = plan.row_chunks;
@@ -452,7 +457,7 @@ extern "C" {
 int spec_verify_attn(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
                      const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
-                     const int32_t* n_q, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                     const int32_t* n_q, void* out, float* lse, void* workspace, size_t workspace_bytes,
                      void* stream) {
   const int st = check_attn_args("spec_verify_attn", d, q, k_cache, v_cache, cache_len, k_blk, v_blk, k_soft,
                                  v_soft, mask_bits, sp_bits, n_q, out, lse);
@@ -471,7 +476,7 @@ int spec_verify_attn(const spec_attn_desc* d, const void* q, const void* k_cache
 int spec_verify_attn_tree(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
                           const void* v_soft, const int32_t* attn_parent, const uint8_t* sp_flag,
-                          const int32_t* n_q, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                          const int32_t* n_q, void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream) {
   static const char* fn = "spec_verify_attn_tree";
   const int st0 = check_desc(d);
@@ -499,7 +504,7 @@ int spec_verify_attn_tree(const spec_attn_desc* d, const void* q, const void* k_
 int spec_verify_attn_msa(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
                          const void* v_soft, const int32_t* tree_parent, const int32_t* n_nodes, int32_t N,
-                         int32_t gamma, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                         int32_t gamma, void* out, float* lse, void* workspace, size_t workspace_bytes,
                          void* stream) {
   static const char* fn = "spec_verify_attn_msa";
   const int st0 = check_desc(d);
@@ -536,7 +541,7 @@ int spec_verify_attn_msa(const spec_attn_desc* d, const void* q, const void* k_c
 int spec_verify_attn_noalloc(const spec_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* cache_len, const void* k_blk, const void* v_blk, const void* k_soft,
                              const void* v_soft, const uint32_t* mask_bits, const uint32_t* sp_bits,
-                             const int32_t* n_q, float* out, float* lse, void* stream) {
+                             const int32_t* n_q, void* out, float* lse, void* stream) {
   const int st = check_attn_args("spec_verify_attn_noalloc", d, q, k_cache, v_cache, cache_len, k_blk, v_blk,
                                  k_soft, v_soft, mask_bits, sp_bits, n_q, out, lse);
   if (st != SPEC_OK) return st;

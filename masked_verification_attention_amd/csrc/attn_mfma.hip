@@ -907,7 +907,16 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const f32x4 v = o[nb][db] * inv;
-        *reinterpret_cast<f32x4*>(a.out + orow * D + 16 * db + 4 * q4) = v;
+        const int64_t at = orow * D + 16 * db + 4 * q4;
+        if (a.out_bf16) {   // rounded to nearest even, 8 bytes per lane
+          typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+          bf16x4v w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = (__bf16)v[i];
+          *reinterpret_cast<bf16x4v*>(static_cast<__bf16*>(a.out) + at) = w;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + at) = v;
+        }
       }
       if (q4 == 0 && a.lse != nullptr)
         a.lse[orow] = row_ok[nb] ? (mrun[nb] + fast_log2(lsum)) * 0.69314718055994531f : -INFINITY;

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kValuThreads) void k_attn_valu(AttnArgs a) {
         if (r < a.Tq) {
           const int64_t orow = ((int64_t)b * a.Tq + r) * a.Hq + (int64_t)h * a.G + g;
           const bool ok = row_ok[i] != 0;
-          a.out[orow * D + d] = ok ? osum / lsum : 0.f;
+          static_cast<float*>(a.out)[orow * D + d] = ok ? osum / lsum : 0.f;   // fp32 inputs: fp32 out
           if (d == 0 && a.lse != nullptr)
             a.lse[orow] = ok ? (M + fast_log2(lsum)) * 0.69314718055994531f : -INFINITY;
         }
@@ -313,7 +313,17 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
       lse = (M + fast_log2(lsum)) * 0.69314718055994531f;
     }
   }
-  *reinterpret_cast<float4*>(a.out + orow * a.D + dq * 4) = res;
+  if (a.out_bf16) {   // rounded to nearest even
+    typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+    bf16x4v w;
+    w[0] = (__bf16)res.x;
+    w[1] = (__bf16)res.y;
+    w[2] = (__bf16)res.z;
+    w[3] = (__bf16)res.w;
+    *reinterpret_cast<bf16x4v*>(static_cast<__bf16*>(a.out) + orow * a.D + dq * 4) = w;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow * a.D + dq * 4) = res;
+  }
   if (dq == 0 && a.lse != nullptr) a.lse[orow] = lse;
 }
 

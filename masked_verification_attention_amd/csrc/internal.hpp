@@ -27,7 +27,8 @@ struct AttnArgs {
   const uint32_t* mask_bits;
   const uint32_t* sp_bits;
   const int32_t* n_q;
-  float* out;
+  void* out;                        // float32, or bf16 when out_bf16
+  int out_bf16;
   float* lse;
   // split-KV partials (only when n_split > 1):
   //   part_o  [n_split][B][Hkv][R][D]  unnormalised accumulators

@@ -55,7 +55,7 @@ class VerifyStep:
     def __init__(self, cfg: VerifyConfig, x: Dict[str, np.ndarray], device="cuda", kv_splits: int = 0,
                  scale: float = 0.0, max_depth: Optional[int] = None, layout: str = "blhd",
                  accept: str = "greedy", threshold: float = 1e-3, draft_prob=None, uniform=None,
-                 fused_mask: Optional[bool] = None):
+                 fused_mask: Optional[bool] = None, out_dtype: str = "f32"):
         """``layout`` of the K/V cache in HBM: "blhd" = [B, lmax, Hkv, D] (token-major, the
         generator's order), "bhld" = [B, Hkv, lmax, D] (head-major), or "bhld_vt" = K head-major
         and V in transposed 32-key tiles [B, Hkv, lmax/32, D, 32] (SPEC_V_TILE32; lmax is
@@ -67,7 +67,9 @@ class VerifyStep:
         ``uniform`` arrays [B, T]).  ``fused_mask``: ``run()`` builds the block mask inside the
         attention launch (spec_verify_attn_tree) instead of with spec_build_mask first; by
         default wherever it applies (bf16 inputs); multi-stream workloads use
-        spec_verify_attn_msa, which does not write n_q (build_mask() does)."""
+        spec_verify_attn_msa, which does not write n_q (build_mask() does).  ``out_dtype``
+        of the attention output: "f32", or "bf16" (bf16 inputs only: the float32 result
+        rounded to nearest even)."""
         self.cfg = cfg
         self.device = torch.device(device)
         dt = cfg.dtype
@@ -127,7 +129,11 @@ class VerifyStep:
         i32 = dict(dtype=torch.int32, device=dev)
         self.mask_bits = torch.zeros(self.B, self.Tq, self.W, **i32)
         self.sp_bits = torch.zeros(self.B, self.W, **i32)
-        self.out = torch.empty(self.B, self.Tq, cfg.Hq, cfg.D, dtype=torch.float32, device=dev)
+        if out_dtype not in ("f32", "bf16"):
+            raise ValueError(out_dtype)
+        self.out_dtype = out_dtype
+        self.out = torch.empty(self.B, self.Tq, cfg.Hq, cfg.D,
+                               dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32, device=dev)
         self.lse = torch.empty(self.B, self.Tq, cfg.Hq, dtype=torch.float32, device=dev)
         self.argmax = torch.empty(self.B, self.T, **i32)
         self.out_len = torch.empty(self.B, **i32)
@@ -158,7 +164,8 @@ class VerifyStep:
                    else (Hkv * self.lmax * D, D, self.lmax * D))
         self.desc = bd.make_desc(self.B, self.Tq, cfg.Hq, Hkv, D, cfg.S, DTYPE_CODE[dt], self.lmax,
                                  strides, scale=scale, kv_splits=kv_splits,
-                                 v_layout=bd.SPEC_V_TILE32 if layout == "bhld_vt" else bd.SPEC_V_ROWS)
+                                 v_layout=bd.SPEC_V_TILE32 if layout == "bhld_vt" else bd.SPEC_V_ROWS,
+                                 out_dtype=DTYPE_CODE[out_dtype])
         self.ws_bytes = bd.spec_verify_attn_workspace(self.desc)
         self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
                           if self.ws_bytes else None)

@@ -98,6 +98,8 @@ void descriptor_refusals() {
       {[](spec_attn_desc& d) {
          d.v_layout = SPEC_V_TILE32; d.lmax = 4150; d.kv_stride_l = d.D; d.kv_stride_h = 4160 * d.D;
        }, SPEC_EINVAL},                                                                 // lmax % 32
+      {[](spec_attn_desc& d) { d.out_dtype = 5; }, SPEC_EINVAL},
+      {[](spec_attn_desc& d) { d.dtype = SPEC_F32; d.out_dtype = SPEC_BF16; }, SPEC_EUNSUPPORTED},
       {[](spec_attn_desc& d) { d.scale = NAN; }, SPEC_EINVAL},
       {[](spec_attn_desc& d) { d.scale = -1.f; }, SPEC_EINVAL},
       {[](spec_attn_desc& d) { d.B = 70000; d.Hkv = 1; d.Hq = 1; }, SPEC_EUNSUPPORTED},  // B * Hkv > 65535

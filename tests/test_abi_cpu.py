@@ -251,6 +251,24 @@ def test_noalloc_scratch_size_matches_header():
     assert m and (int(m.group(1)) << int(m.group(2))) == bd.SPEC_NOALLOC_SCRATCH_BYTES
 
 
+def test_out_dtype_validation():
+    ok_desc = good_desc()
+    ok_desc.out_dtype = bd.SPEC_BF16
+    assert bd.spec_verify_attn_workspace(ok_desc) > 0
+    cases = [
+        (dict(), 5, bd.SPEC_EINVAL, "out_dtype"),                            # not a dtype
+        (dict(), -1, bd.SPEC_EINVAL, "out_dtype"),
+        (dict(dtype=bd.SPEC_F32), bd.SPEC_BF16, bd.SPEC_EUNSUPPORTED, "bf16"),  # bf16 out of f32 inputs
+    ]
+    for kw, od, status, word in cases:
+        desc = good_desc(**kw)
+        desc.out_dtype = od
+        assert bd.spec_verify_attn_workspace(desc) == 0
+        with pytest.raises(bd.SpecError) as e:
+            attn(desc)
+        assert e.value.status == status and word in str(e.value), (kw, od, str(e.value))
+
+
 def test_v_layout_validation():
     hm = dict(lmax=4160, strides=(8 * 4160 * 128, 128, 4160 * 128))
     ok_desc = good_desc(**hm)

@@ -32,6 +32,8 @@ def test_algorithmic_bytes_by_parts():
     expect = (kv + S * Hkv * D * 4 + B * Tq * Hq * D * 2 + B * Tq * Hkv * D * 4 + B * Tq * W * 4 + B * W * 4
               + B * Tq * Hq * (D + 1) * 4)
     assert bench.attention_algorithmic_bytes(cfg, x) == expect
+    # a bf16 output halves the output values; the lse stays fp32
+    assert bench.attention_algorithmic_bytes(cfg, x, out_es=2) == expect - B * Tq * Hq * D * 2
 
 
 def test_flops_count_visible_pairs():
@@ -70,9 +72,10 @@ def test_counter_summary_scales_by_the_copy(tmp_path):
 
 def test_counter_record_is_keyed_on_workload_and_kernel_source(tmp_path, monkeypatch):
     rec = {"workload": "c4_tree_3b", "kernel_src_sha256": "0" * 64, "traffic_bytes_per_launch": 1.0, "taken": "x"}
-    path = tmp_path / "attn_mfma_c4_tree_3b_counters.json"
+    path = tmp_path / "attn_mfma_c4_tree_3b_f32_counters.json"
     path.write_text(json.dumps(rec))
-    monkeypatch.setattr(bench, "counters_file", lambda w: str(tmp_path / f"attn_mfma_{w}_counters.json"))
+    monkeypatch.setattr(bench, "counters_file",
+                        lambda w, out="f32": str(tmp_path / f"attn_mfma_{w}_{out}_counters.json"))
     assert bench.counters_traffic("c4_tree_3b") == (None, None)          # stale source hash
     import hashlib
     rec["kernel_src_sha256"] = hashlib.sha256(open(bench.ATTN_SRC, "rb").read()).hexdigest()
@@ -80,6 +83,8 @@ def test_counter_record_is_keyed_on_workload_and_kernel_source(tmp_path, monkeyp
     traffic, src = bench.counters_traffic("c4_tree_3b")
     assert traffic == 1.0 and src["kernel_src_sha256"] == rec["kernel_src_sha256"] and src["taken"] == "x"
     assert bench.counters_traffic("c3_confu_8b") == (None, None)         # no record for that workload
+    (tmp_path / "attn_mfma_c4_tree_3b_bf16_counters.json").write_text(json.dumps(rec))
+    assert bench.counters_traffic("c4_tree_3b", "bf16") == (None, None)  # taken with the fp32 output
 
 
 def test_argmax_bytes_count_node_rows():
