@@ -797,6 +797,7 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     // step's loads, the scores and the hand-off barrier; the V fragments are
     // read only once the K fragments are dead (both at once would overflow the
     // registers here), then P*V and the softmax.
+    bool skip_prev = false;   // the group's previous tile was skipped (no P*V for it)
     auto tail_step = [&](int s) __attribute__((always_inline)) {
       begin_step(s);
       const TileSrc src = tile_src(s + C::P / 2);
@@ -816,9 +817,18 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       // longer one in these steps -- runs the unmasked softmax.
       int seg = 0, lim = 0;
       uint32_t mw[NB];
+      bool skip = false;
       if (has_t) {   // then has_p as well
         tile_kind(t, seg, lim);
         read_mask(t, seg, mw);
+        if (seg == 2) {
+          uint32_t seen = 0;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) seen |= mw[nb];
+          skip = !__any(seen != 0u);
+        }
+      }
+      if (has_t && !skip) {
         bf16x8 kf[2][DC];
         read_k(t, kf);
         __builtin_amdgcn_sched_barrier(0);
@@ -834,23 +844,40 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       block_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (has_p) {
+      if (has_p && !skip_prev) {
         bf16x8 vf[DB];
         read_pv(vf);
         pv(vf);
       }
-      if (has_t) {
+      if (has_t && !skip) {
         __builtin_amdgcn_s_setprio(1);
         softmax_biased(seg, lim, mw);
         __builtin_amdgcn_s_setprio(0);
       }
+      skip_prev = skip;
     };
     const int nfull = (ke - ks) / C::TK;
     const int s_hot_end = (nfull - grp + 1) / 2;   // steps whose own tile is a full prefix tile
+    // A wave none of whose rows exists (past the kv-head's rows, or past the
+    // request's queries) only loads its share of the tiles and keeps the
+    // barriers: its SIMD and the LDS are then free for the other waves.  Its
+    // rows' accumulators stay zero, which is what the epilogue writes for them.
+    bool has_row = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) has_row = has_row || row_ok[nb];
+    const bool idle = !__any(has_row);
     if (grp == 1) block_barrier();
-    generic_step(0);
-    for (int s = 1; s < s_hot_end; ++s) hot_step(s);
-    for (int s = max(1, s_hot_end); s <= nsteps; ++s) tail_step(s);
+    if (idle) {
+      for (int s = 0; s <= nsteps; ++s) {
+        begin_step(s);
+        issue_step(s + C::P / 2);
+        block_barrier();
+      }
+    } else {
+      generic_step(0);
+      for (int s = 1; s < s_hot_end; ++s) hot_step(s);
+      for (int s = max(1, s_hot_end); s <= nsteps; ++s) tail_step(s);
+    }
     if (grp == 0) block_barrier();
     __builtin_amdgcn_s_waitcnt(0);
   }
