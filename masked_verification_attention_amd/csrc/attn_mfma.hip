@@ -117,6 +117,12 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
     b = bh / a.Hkv;
     h = bh % a.Hkv;
   }
+  // uniform values in scalar registers: the request's scalars then come by
+  // scalar loads, which no wait for the tile loads below has to cover
+  b = __builtin_amdgcn_readfirstlane(b);
+  h = __builtin_amdgcn_readfirstlane(h);
+  chunk_id = __builtin_amdgcn_readfirstlane(chunk_id);
+  split = __builtin_amdgcn_readfirstlane(split);
 
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int grp = wave >> 2;          // key-tile parity this wave computes
@@ -125,10 +131,77 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  const int L = (int)min<int64_t>(max(a.cache_len[b], 0), a.lmax);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_char*)ring;
+  // The request's prefix length and row count (n_q, or for multi-stream rows
+  // the node count): scalar loads issued here, used after the setup loads.
+  const bool msa = a.mask_mode == MASK_MSA;
+  const int len_raw = a.cache_len[b];
+  const int cnt = (msa ? a.n_nodes : a.n_q)[b];
+  // ---- setup loads.  They need only the workgroup's request, kv-head and
+  // rows, so they go out before the lengths are waited for.  Everything a wave needs before the first step comes
+  // through the same direct-to-LDS path as the tiles, ahead of them, so that
+  // no compiler-generated wait (which would count the tile loads too) stands
+  // between the setup and the first step: the workgroup's query rows (staged
+  // in V slots 4..7, which the tile stream first writes at step P/2), the mask
+  // words of its rows and the request's soft-prompt words.  Rows past the end
+  // or past the request's queries read an in-range row; the values are not used.
+  // When the mask is built here (from the parent array, or from the node tree
+  // of multi-stream rows), the parents and soft-prompt flags come instead, by
+  // the same path (a flag byte lands as a zero-extended word), into a slot that
+  // the tile stream first writes at step P/2; after the setup barrier each
+  // thread walks one row's chain there (below).
+  const bool tree = a.mask_mode != MASK_WORDS;
+  const int nchain = msa ? a.msa_N : a.Tq;    // parents: one per tree node or block row
+  char* const aux_l = ring + 6 * C::TILEB;                                               // K slot 6
+  int32_t* const par_l = reinterpret_cast<int32_t*>(aux_l);                              // [nchain]
+  uint32_t* const spf_l = reinterpret_cast<uint32_t*>(aux_l + SPEC_MAX_TQ * 4);            // [Tq]
+  static_assert(SPEC_MAX_TQ * 8 <= C::TILEB, "parents and flags fit in one slot");
+  static_assert(C::ROWS <= C::kThreads, "one workgroup row per thread");
+  const bool has_flags = !msa && a.sp_flag != nullptr;
+  const int row0 = chunk_id * C::ROWS;
+  constexpr int QOPS = C::ROWS * D * 2 / 1024 / C::kWaves;   // 1 KB query loads per wave
+  static_assert(QOPS >= 1 && QOPS * 1024 * C::kWaves == C::ROWS * D * 2, "query staging split");
+  static_assert(C::ROWS * D * 2 <= 4 * C::TILEB, "query rows fit in V slots 4..7");
+  const char* const qstage = ring + (C::NSK + 4) * C::TILEB;
+  {
+    // 16-byte chunk c of stage row rr sits at position c ^ (rr mod CH)
+#pragma unroll
+    for (int jq = 0; jq < QOPS; ++jq) {
+      const int n = (wave * QOPS + jq) * 64 + lane;
+      const int rr = n / C::CH, c = (n % C::CH) ^ (rr & (C::CH - 1));
+      const int m = row0 + rr;
+      const int r = min(m / a.G, a.Tq - 1), g = m % a.G;
+      dma16(ring_lds + (C::NSK + 4) * C::TILEB + (wave * QOPS + jq) * 1024,
+            static_cast<const char*>(a.q) + ((((int64_t)b * a.Tq + r) * a.Hq + h * a.G + g) * D + 8 * c) * 2);
+    }
+    if (tree) {
+      // entries 64 k .. 64 k + 63 by wave k (thread r's entry comes with its own wave's
+      // loads); lanes past the end repeat the last entry
+      if (wave * 64 < nchain) {
+        const int r = min(wave * 64 + lane, nchain - 1);
+        const uint32_t aux = (uint32_t)(uintptr_t)(lds_char*)aux_l;   // par_l, then spf_l
+        dma4(aux + wave * 256, a.attn_parent + (int64_t)b * nchain + r);
+        if (has_flags) dma1(aux + SPEC_MAX_TQ * 4 + wave * 256, a.sp_flag + (int64_t)b * a.Tq + r);
+      }
+    } else {
+      const uint32_t mask_addr = (uint32_t)(uintptr_t)(lds_char*)(char*)mask_lds;
+      const int nmw = C::ROWS * a.W / 64;   // ROWS is a multiple of 64: whole wave loads
+      for (int k = wave; k < nmw; k += C::kWaves) {
+        const int n = k * 64 + lane;
+        const int r = min((row0 + n / a.W) / a.G, a.Tq - 1);
+        dma4(mask_addr + k * 256, a.mask_bits + ((int64_t)b * a.Tq + r) * a.W + n % a.W);
+      }
+      if (a.S > 0 && wave == C::kWaves - 1)
+        dma4((uint32_t)(uintptr_t)(lds_char*)(char*)sp_lds, a.sp_bits + (int64_t)b * a.W + min(lane, a.W - 1));
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int L = (int)min<int64_t>(max(len_raw, 0), a.lmax);
   // multi-stream rows: n nodes, each with its main row and gamma stream rows
-  const int msa_n = a.mask_mode == MASK_MSA ? clampi(a.n_nodes[b], 0, a.msa_N) : 0;
-  const int nq = a.mask_mode == MASK_MSA ? min(msa_n * (1 + a.msa_gamma), a.Tq) : clampi(a.n_q[b], 0, a.Tq);
+  const int msa_n = msa ? clampi(cnt, 0, a.msa_N) : 0;
+  const int nq = msa ? min(msa_n * (1 + a.msa_gamma), a.Tq) : clampi(cnt, 0, a.Tq);
   // split boundaries on 32-key multiples, so a split's prefix tiles are the cache's tiles
   const int keys_per_split = (((L + a.n_split - 1) / a.n_split) + C::TK - 1) / C::TK * C::TK;
   const int ks = min(L, split * keys_per_split);
@@ -153,7 +226,6 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
   const bool load_v = (gw * C::LPS) / C::LPT >= 1;   // first half of the group loads K, second V
   const int lrow = lane / C::CH;               // key row within the wave's 1 KB load
   const int lpos = lane % C::CH;               // chunk position the lane fills
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_char*)ring;
   const char* const kring = ring;
   const char* const vring = ring + C::NSK * C::TILEB;
   int lane_row[C::LPS], lane_off[C::LPS], lane_dst[C::LPS];
@@ -222,65 +294,6 @@ __global__ __launch_bounds__(512) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < C::LPS; ++j) issue_one(r, j);
   };
-
-  // ---- setup loads.  Everything a wave needs before the first step comes
-  // through the same direct-to-LDS path as the tiles, ahead of them, so that
-  // no compiler-generated wait (which would count the tile loads too) stands
-  // between the setup and the first step: the workgroup's query rows (staged
-  // in V slots 4..7, which the tile stream first writes at step P/2), the mask
-  // words of its rows and the request's soft-prompt words.  Rows past the end
-  // or past the request's queries read an in-range row; the values are not used.
-  // When the mask is built here (from the parent array, or from the node tree
-  // of multi-stream rows), the parents and soft-prompt flags come instead, by
-  // the same path (a flag byte lands as a zero-extended word), into a slot that
-  // the tile stream first writes at step P/2; after the setup barrier each
-  // thread walks one row's chain there (below).
-  const bool tree = a.mask_mode != MASK_WORDS;
-  const bool msa = a.mask_mode == MASK_MSA;
-  const int nchain = msa ? a.msa_N : a.Tq;    // parents: one per tree node or block row
-  char* const aux_l = ring + 6 * C::TILEB;                                               // K slot 6
-  int32_t* const par_l = reinterpret_cast<int32_t*>(aux_l);                              // [nchain]
-  uint32_t* const spf_l = reinterpret_cast<uint32_t*>(aux_l + SPEC_MAX_TQ * 4);            // [Tq]
-  static_assert(SPEC_MAX_TQ * 8 <= C::TILEB, "parents and flags fit in one slot");
-  static_assert(C::ROWS <= C::kThreads, "one workgroup row per thread");
-  const bool has_flags = !msa && a.sp_flag != nullptr;
-  const int row0 = chunk_id * C::ROWS;
-  constexpr int QOPS = C::ROWS * D * 2 / 1024 / C::kWaves;   // 1 KB query loads per wave
-  static_assert(QOPS >= 1 && QOPS * 1024 * C::kWaves == C::ROWS * D * 2, "query staging split");
-  static_assert(C::ROWS * D * 2 <= 4 * C::TILEB, "query rows fit in V slots 4..7");
-  const char* const qstage = ring + (C::NSK + 4) * C::TILEB;
-  {
-    // 16-byte chunk c of stage row rr sits at position c ^ (rr mod CH)
-#pragma unroll
-    for (int jq = 0; jq < QOPS; ++jq) {
-      const int n = (wave * QOPS + jq) * 64 + lane;
-      const int rr = n / C::CH, c = (n % C::CH) ^ (rr & (C::CH - 1));
-      const int m = row0 + rr;
-      const int r = min(m / a.G, a.Tq - 1), g = m % a.G;
-      dma16(ring_lds + (C::NSK + 4) * C::TILEB + (wave * QOPS + jq) * 1024,
-            static_cast<const char*>(a.q) + ((((int64_t)b * a.Tq + r) * a.Hq + h * a.G + g) * D + 8 * c) * 2);
-    }
-    if (tree) {
-      // entries 64 k .. 64 k + 63 by wave k (thread r's entry comes with its own wave's
-      // loads); lanes past the end repeat the last entry
-      if (wave * 64 < nchain) {
-        const int r = min(wave * 64 + lane, nchain - 1);
-        const uint32_t aux = (uint32_t)(uintptr_t)(lds_char*)aux_l;   // par_l, then spf_l
-        dma4(aux + wave * 256, a.attn_parent + (int64_t)b * nchain + r);
-        if (has_flags) dma1(aux + SPEC_MAX_TQ * 4 + wave * 256, a.sp_flag + (int64_t)b * a.Tq + r);
-      }
-    } else {
-      const uint32_t mask_addr = (uint32_t)(uintptr_t)(lds_char*)(char*)mask_lds;
-      const int nmw = C::ROWS * a.W / 64;   // ROWS is a multiple of 64: whole wave loads
-      for (int k = wave; k < nmw; k += C::kWaves) {
-        const int n = k * 64 + lane;
-        const int r = min((row0 + n / a.W) / a.G, a.Tq - 1);
-        dma4(mask_addr + k * 256, a.mask_bits + ((int64_t)b * a.Tq + r) * a.W + n % a.W);
-      }
-      if (a.S > 0 && wave == C::kWaves - 1)
-        dma4((uint32_t)(uintptr_t)(lds_char*)(char*)sp_lds, a.sp_bits + (int64_t)b * a.W + min(lane, a.W - 1));
-    }
-  }
 
   // The first steps' tiles follow; their HBM latency overlaps the setup's.
   if (nt > 0) {
